@@ -1,0 +1,13 @@
+"""CPU oracle for the DSA sparse MLA forward.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import this package:
+only the test suite, the smoke check and the CPU-baseline leg of the benchmark
+call it. It shares no code with the HIP library.
+"""
+from .sparse_mla_ref import (  # noqa: F401
+    DQK,
+    DV,
+    map_paged_indices,
+    sparse_mla_fwd_ref,
+    sparse_mla_fwd_paged_ref,
+)
