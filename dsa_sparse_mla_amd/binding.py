@@ -1,0 +1,200 @@
+"""ctypes binding of libdsa_sparse_mla.so: argument marshalling only.
+
+Every step of the forward runs in the HIP kernels behind the C ABI
+(include/dsa_sparse_mla.h). torch supplies device memory and the current
+stream, nothing else. If the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_sparse_mla.so")
+DQK = 576
+DV = 512
+
+_lock = threading.Lock()
+_lib = None
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error", 4: "workspace too small"}
+
+
+class DsaError(RuntimeError):
+    """A non-zero status from the C ABI."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib().dsa_status_string(status).decode()} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once. torch is imported first, so the library binds to
+    the HIP runtime torch already mapped (both carry soname libamdhip64.so.7)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python dsa_sparse_mla_amd/build.py` "
+                "(or __graft_entry__.build()) first")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+        L.dsa_sparse_mla_fwd.restype = ctypes.c_int
+        L.dsa_sparse_mla_fwd.argtypes = [
+            vp, i64, i64,            # q
+            vp, i64, i64,            # kv, row stride, num_kv
+            vp, i64,                 # indices
+            i64, i32, i32, f32,      # T, H, topk, sm_scale
+            vp, i64, i64,            # out
+            vp, i64,                 # lse
+            i32, vp, i64,            # num_splits, workspace, bytes
+            vp]                      # stream
+        L.dsa_sparse_mla_fwd_paged.restype = ctypes.c_int
+        L.dsa_sparse_mla_fwd_paged.argtypes = [
+            vp, i64, i64,            # q
+            vp, i64, i64, i64, i32,  # kv_pages, page stride, row stride, num_pages, page_size
+            vp, i64, i32, vp,        # page_table, stride, max_pages, seq_lens
+            vp, i64,                 # indices
+            i32, i32, i32, i32, f32,  # num_seqs, q_per_seq, H, topk, sm_scale
+            vp, i64, i64,            # out
+            vp, i64,                 # lse
+            i32, vp, i64,            # num_splits, workspace, bytes
+            vp]                      # stream
+        L.dsa_sparse_mla_workspace_size.restype = ctypes.c_int
+        L.dsa_sparse_mla_workspace_size.argtypes = [i64, i32, i32, i32,
+                                                    ctypes.POINTER(i32), ctypes.POINTER(i64)]
+        L.dsa_status_string.restype = ctypes.c_char_p
+        L.dsa_status_string.argtypes = [ctypes.c_int]
+        L.dsa_device_supported.restype = ctypes.c_int
+        L.dsa_device_supported.argtypes = [ctypes.c_int]
+        L.dsa_version.restype = ctypes.c_int
+        L.dsa_version.argtypes = []
+        _lib = L
+        return _lib
+
+
+def workspace_size(num_tokens: int, num_heads: int, topk: int, num_splits: int = 0):
+    """(splits, bytes) that a forward call with these sizes uses on the current device."""
+    s = ctypes.c_int32(0)
+    b = ctypes.c_int64(0)
+    st = lib().dsa_sparse_mla_workspace_size(num_tokens, num_heads, topk, num_splits,
+                                             ctypes.byref(s), ctypes.byref(b))
+    if st != 0:
+        raise DsaError(st, "dsa_sparse_mla_workspace_size")
+    return s.value, b.value
+
+
+def _check(t: torch.Tensor, name: str, dtype, ndim: int, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dim() and t.stride(-1) != 1:
+        raise ValueError(f"{name} needs a contiguous last dimension")
+
+
+def _outputs(q, T, H, out, lse):
+    if out is None:
+        out = torch.empty((T, H, DV), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _check(out, "out", torch.bfloat16, 3, q.device)
+    _check(lse, "lse", torch.float32, 2, q.device)
+    if tuple(out.shape) != (T, H, DV) or tuple(lse.shape) != (T, H):
+        raise ValueError("out must be [T, H, 512] and lse [T, H]")
+    return out, lse
+
+
+def _workspace(q, T, H, topk, num_splits, workspace):
+    _, need = workspace_size(T, H, topk, num_splits)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def sparse_mla_fwd(q, kv, indices, sm_scale, out=None, lse=None, num_splits=0, workspace=None):
+    """Sparse MLA forward over flat KV (packed/varlen prefill).
+
+    q [T,H,576] bf16, kv [N,576] bf16, indices [T,topk] int32 (row ids; -1 or
+    any out-of-range value is padding). Returns (out [T,H,512] bf16, lse [T,H] fp32).
+    Runs on torch's current stream of q's device.
+    """
+    dev = q.device
+    _check(q, "q", torch.bfloat16, 3, dev)
+    _check(kv, "kv", torch.bfloat16, 2, dev)
+    _check(indices, "indices", torch.int32, 2, dev)
+    T, H, D = q.shape
+    if D != DQK or kv.shape[1] != DQK:
+        raise ValueError("q and kv rows must be 576 wide")
+    if indices.shape[0] != T:
+        raise ValueError("indices must have one row per token")
+    topk = indices.shape[1]
+    out, lse = _outputs(q, T, H, out, lse)
+    ws, ws_bytes = _workspace(q, T, H, topk, num_splits, workspace)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib().dsa_sparse_mla_fwd(
+            q.data_ptr(), q.stride(0), q.stride(1),
+            kv.data_ptr(), kv.stride(0), kv.shape[0],
+            indices.data_ptr(), indices.stride(0),
+            T, H, topk, float(sm_scale),
+            out.data_ptr(), out.stride(0), out.stride(1),
+            lse.data_ptr(), lse.stride(0),
+            int(num_splits), ws.data_ptr() if ws is not None else None, ws_bytes,
+            stream)
+    if st != 0:
+        raise DsaError(st, "dsa_sparse_mla_fwd")
+    return out, lse
+
+
+def sparse_mla_fwd_paged(q, kv_pages, page_table, seq_lens, indices, sm_scale, q_per_seq,
+                         out=None, lse=None, num_splits=0, workspace=None):
+    """Sparse MLA forward over a paged bf16 cache (decode), no gather copy.
+
+    q [S*q_per_seq, H, 576] bf16; kv_pages [P, page_size, 576] bf16;
+    page_table [S, max_pages] int32; seq_lens [S] int32; indices
+    [S*q_per_seq, topk] int32 logical positions. Returns (out, lse).
+    """
+    dev = q.device
+    _check(q, "q", torch.bfloat16, 3, dev)
+    _check(kv_pages, "kv_pages", torch.bfloat16, 3, dev)
+    _check(page_table, "page_table", torch.int32, 2, dev)
+    _check(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _check(indices, "indices", torch.int32, 2, dev)
+    T, H, D = q.shape
+    S = page_table.shape[0]
+    if D != DQK or kv_pages.shape[2] != DQK:
+        raise ValueError("q and kv rows must be 576 wide")
+    if seq_lens.shape[0] != S or T != S * q_per_seq or indices.shape[0] != T:
+        raise ValueError("need num_seqs * q_per_seq query tokens and one seq_len per sequence")
+    topk = indices.shape[1]
+    out, lse = _outputs(q, T, H, out, lse)
+    ws, ws_bytes = _workspace(q, T, H, topk, num_splits, workspace)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib().dsa_sparse_mla_fwd_paged(
+            q.data_ptr(), q.stride(0), q.stride(1),
+            kv_pages.data_ptr(), kv_pages.stride(0), kv_pages.stride(1),
+            kv_pages.shape[0], kv_pages.shape[1],
+            page_table.data_ptr(), page_table.stride(0), page_table.shape[1], seq_lens.data_ptr(),
+            indices.data_ptr(), indices.stride(0),
+            S, int(q_per_seq), H, topk, float(sm_scale),
+            out.data_ptr(), out.stride(0), out.stride(1),
+            lse.data_ptr(), lse.stride(0),
+            int(num_splits), ws.data_ptr() if ws is not None else None, ws_bytes,
+            stream)
+    if st != 0:
+        raise DsaError(st, "dsa_sparse_mla_fwd_paged")
+    return out, lse

@@ -1,0 +1,280 @@
+// C ABI and launch layer of the DSA sparse MLA forward (gfx950 only).
+//
+// Every argument is checked on the host before any HIP call, so a bad call
+// returns a status without touching the device. Then the layer picks the
+// head-tile / key-group shape of the workgroup from the head count, picks the
+// split of each index row, and enqueues the kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "dsa_sparse_mla.h"
+#include "fwd_kernel.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  int cus = 0;
+  bool gfx950 = false;
+  bool ok = false;
+};
+
+DeviceInfo g_dev[kMaxDevices];
+std::once_flag g_dev_once[kMaxDevices];
+
+const DeviceInfo* device_info(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_dev_once[dev], [dev] {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
+    g_dev[dev].cus = prop.multiProcessorCount;
+    g_dev[dev].gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_dev[dev].ok = true;
+  });
+  return g_dev[dev].ok ? &g_dev[dev] : nullptr;
+}
+
+int current_device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const DeviceInfo* d = device_info(dev);
+  return d ? d->cus : 256;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Split choice. Each workgroup gathers at most kSegment entries. With few
+// tokens and long rows, more workgroups per token fill the 256 CUs; short
+// problems are not split (the merge pass would cost more than it saves).
+int choose_splits(int64_t T, int32_t topk, int32_t requested, int cus) {
+  const int smin = (topk + dsa::kSegment - 1) / dsa::kSegment;
+  if (requested > 0) return requested;
+  int s = smin;
+  if (T * (int64_t)topk >= (int64_t)256 * 1024) {
+    while (T * s < 4LL * cus && (int64_t)s * 2 * 128 <= topk && s < 64) s *= 2;
+  }
+  return s;
+}
+
+int check_splits(int64_t T, int32_t H, int32_t topk, int32_t requested, int* splits, int* seg_len,
+                 int64_t* ws_bytes) {
+  const int smin = (topk + dsa::kSegment - 1) / dsa::kSegment;
+  if (requested < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (requested > 0 && (requested < smin || requested > topk)) return DSA_ERR_INVALID_ARGUMENT;
+  const int s = choose_splits(T, topk, requested, requested > 0 ? 256 : current_device_cus());
+  const int seg = (topk + s - 1) / s;  // <= kSegment because s >= smin; a split may own no entry
+  *splits = s;
+  *seg_len = seg;
+  *ws_bytes = s > 1 ? T * (int64_t)s * H * (int64_t)(dsa::kDv + 2) * 4 : 0;
+  return DSA_OK;
+}
+
+int check_common(const void* q, int64_t q_st, int64_t q_sh, const int32_t* idx, int64_t idx_st,
+                 int64_t T, int32_t H, int32_t topk, const void* out, int64_t o_st, int64_t o_sh,
+                 const float* lse, int64_t lse_st) {
+  if (T < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (H < 1 || H > DSA_MAX_HEADS || topk < 1 || topk > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+  if (T == 0) return DSA_OK;
+  if (!q || !idx || !out || !lse) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(idx, 4) || !aligned(lse, 4))
+    return DSA_ERR_INVALID_ARGUMENT;
+  if (q_st < 0 || q_sh < 0 || o_st < 0 || o_sh < 0 || idx_st < 0 || lse_st < 0)
+    return DSA_ERR_INVALID_ARGUMENT;
+  if (q_st % 8 || q_sh % 8 || o_st % 8 || o_sh % 8) return DSA_ERR_INVALID_ARGUMENT;
+  if (T > 1 && (q_st == 0 || o_st == 0 || idx_st < topk || lse_st < H)) return DSA_ERR_INVALID_ARGUMENT;
+  if (H > 1 && (q_sh < DSA_DQK || o_sh < DSA_DV)) return DSA_ERR_INVALID_ARGUMENT;
+  return DSA_OK;
+}
+
+int device_check() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_HIP;
+  const DeviceInfo* d = device_info(dev);
+  if (!d) return DSA_ERR_HIP;
+  return d->gfx950 ? DSA_OK : DSA_ERR_UNSUPPORTED;
+}
+
+template <bool PAGED>
+int launch(const dsa::FwdArgs& args, hipStream_t stream) {
+  const int H = args.num_heads;
+  const dim3 grid((unsigned)(args.num_tokens * args.splits));
+  if (H <= 16) {
+    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<1, 4, PAGED>), grid, dim3(256), 0, stream, args);
+  } else if (H <= 32) {
+    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<2, 2, PAGED>), grid, dim3(256), 0, stream, args);
+  } else if (H <= 64) {
+    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<4, 1, PAGED>), grid, dim3(256), 0, stream, args);
+  } else {
+    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<8, 1, PAGED>), grid, dim3(512), 0, stream, args);
+  }
+  if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
+  if (args.splits > 1) {
+    const int64_t pairs = args.num_tokens * (int64_t)H;
+    hipLaunchKernelGGL(dsa::sparse_mla_combine_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0,
+                       stream, args);
+    if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
+  }
+  return DSA_OK;
+}
+
+int fill_outputs_and_splits(dsa::FwdArgs& a, const void* q, int64_t q_st, int64_t q_sh,
+                            const int32_t* idx, int64_t idx_st, int64_t T, int32_t H, int32_t topk,
+                            float sm_scale, void* out, int64_t o_st, int64_t o_sh, float* lse,
+                            int64_t lse_st, int32_t num_splits, void* ws, int64_t ws_bytes) {
+  if (!std::isfinite(sm_scale)) return DSA_ERR_INVALID_ARGUMENT;
+  int splits = 1, seg = topk;
+  int64_t need = 0;
+  int st = check_splits(T, H, topk, num_splits, &splits, &seg, &need);
+  if (st != DSA_OK) return st;
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return DSA_ERR_WORKSPACE;
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_st = q_st;
+  a.q_sh = q_sh;
+  a.idx = idx;
+  a.idx_st = idx_st;
+  a.num_tokens = T;
+  a.num_heads = H;
+  a.topk = topk;
+  a.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  a.out = static_cast<uint16_t*>(out);
+  a.o_st = o_st;
+  a.o_sh = o_sh;
+  a.lse = lse;
+  a.lse_st = lse_st;
+  a.splits = splits;
+  a.seg_len = seg;
+  if (splits > 1) {
+    a.part_o = static_cast<float*>(ws);
+    a.part_ml = a.part_o + T * (int64_t)splits * H * dsa::kDv;
+  }
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_sparse_mla_workspace_size(int64_t num_tokens, int32_t num_heads, int32_t topk,
+                                  int32_t num_splits, int32_t* splits_out, int64_t* bytes_out) {
+  if (!bytes_out) return DSA_ERR_INVALID_ARGUMENT;
+  if (num_tokens < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (num_heads < 1 || num_heads > DSA_MAX_HEADS || topk < 1 || topk > DSA_MAX_TOPK)
+    return DSA_ERR_UNSUPPORTED;
+  int splits = 1, seg = topk;
+  int64_t need = 0;
+  int st = check_splits(num_tokens, num_heads, topk, num_splits, &splits, &seg, &need);
+  if (st != DSA_OK) return st;
+  if (splits_out) *splits_out = splits;
+  *bytes_out = need;
+  return DSA_OK;
+}
+
+int dsa_sparse_mla_fwd(const void* q, int64_t q_stride_tok, int64_t q_stride_head, const void* kv,
+                       int64_t kv_stride_row, int64_t num_kv, const int32_t* indices,
+                       int64_t idx_stride_tok, int64_t num_tokens, int32_t num_heads, int32_t topk,
+                       float sm_scale, void* out, int64_t out_stride_tok, int64_t out_stride_head,
+                       float* lse, int64_t lse_stride_tok, int32_t num_splits, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
+  int st = check_common(q, q_stride_tok, q_stride_head, indices, idx_stride_tok, num_tokens, num_heads,
+                        topk, out, out_stride_tok, out_stride_head, lse, lse_stride_tok);
+  if (st != DSA_OK || num_tokens == 0) return st;
+  if (num_kv < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (num_kv > 0) {
+    if (!kv || !aligned(kv, 16) || kv_stride_row % 8 || kv_stride_row < (num_kv > 1 ? DSA_DQK : 0))
+      return DSA_ERR_INVALID_ARGUMENT;
+    // row offsets are kept as 32-bit counts of 16-byte granules
+    const int64_t gran = kv_stride_row / 8;
+    if (num_kv > ((int64_t)1 << 32) / (gran > 0 ? gran : 1) - 1) return DSA_ERR_UNSUPPORTED;
+  }
+  dsa::FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  st = fill_outputs_and_splits(a, q, q_stride_tok, q_stride_head, indices, idx_stride_tok, num_tokens,
+                               num_heads, topk, sm_scale, out, out_stride_tok, out_stride_head, lse,
+                               lse_stride_tok, num_splits, workspace, workspace_bytes);
+  if (st != DSA_OK) return st;
+  a.kv = static_cast<const uint8_t*>(kv);
+  a.kv_row_gran = kv_stride_row / 8;
+  a.num_kv = num_kv;
+  st = device_check();
+  if (st != DSA_OK) return st;
+  return launch<false>(a, static_cast<hipStream_t>(stream));
+}
+
+int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                             const void* kv_pages, int64_t kv_stride_page, int64_t kv_stride_row,
+                             int64_t num_pages, int32_t page_size, const int32_t* page_table,
+                             int64_t page_table_stride, int32_t max_pages_per_seq,
+                             const int32_t* seq_lens, const int32_t* indices, int64_t idx_stride_tok,
+                             int32_t num_seqs, int32_t q_per_seq, int32_t num_heads, int32_t topk,
+                             float sm_scale, void* out, int64_t out_stride_tok, int64_t out_stride_head,
+                             float* lse, int64_t lse_stride_tok, int32_t num_splits, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || q_per_seq < 1) return DSA_ERR_INVALID_ARGUMENT;
+  const int64_t T = (int64_t)num_seqs * q_per_seq;
+  int st = check_common(q, q_stride_tok, q_stride_head, indices, idx_stride_tok, T, num_heads, topk, out,
+                        out_stride_tok, out_stride_head, lse, lse_stride_tok);
+  if (st != DSA_OK || T == 0) return st;
+  if (page_size < 1 || page_size > 4096 || (page_size & (page_size - 1))) return DSA_ERR_UNSUPPORTED;
+  if (num_pages < 0 || max_pages_per_seq < 0 || page_table_stride < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (!seq_lens || !aligned(seq_lens, 4)) return DSA_ERR_INVALID_ARGUMENT;
+  if (max_pages_per_seq > 0 && (!page_table || !aligned(page_table, 4))) return DSA_ERR_INVALID_ARGUMENT;
+  if (num_seqs > 1 && max_pages_per_seq > 0 && page_table_stride < max_pages_per_seq)
+    return DSA_ERR_INVALID_ARGUMENT;
+  if (num_pages > 0) {
+    if (!kv_pages || !aligned(kv_pages, 16) || kv_stride_row % 8 || kv_stride_page % 8)
+      return DSA_ERR_INVALID_ARGUMENT;
+    if ((page_size > 1 && kv_stride_row < DSA_DQK) ||
+        (num_pages > 1 && kv_stride_page < (int64_t)page_size * kv_stride_row))
+      return DSA_ERR_INVALID_ARGUMENT;
+    const int64_t page_gran = kv_stride_page / 8;
+    const int64_t span = (num_pages - 1) * page_gran + (int64_t)page_size * (kv_stride_row / 8);
+    if (span >= ((int64_t)1 << 32)) return DSA_ERR_UNSUPPORTED;
+  }
+  dsa::FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  st = fill_outputs_and_splits(a, q, q_stride_tok, q_stride_head, indices, idx_stride_tok, T, num_heads,
+                               topk, sm_scale, out, out_stride_tok, out_stride_head, lse, lse_stride_tok,
+                               num_splits, workspace, workspace_bytes);
+  if (st != DSA_OK) return st;
+  a.kv = static_cast<const uint8_t*>(kv_pages);
+  a.kv_row_gran = kv_stride_row / 8;
+  a.kv_page_gran = kv_stride_page / 8;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  a.page_shift = shift;
+  a.page_mask = page_size - 1;
+  a.page_table = page_table;
+  a.pt_stride = page_table_stride;
+  a.max_pages = max_pages_per_seq;
+  a.seq_lens = seq_lens;
+  a.q_per_seq = q_per_seq;
+  a.num_pages = num_pages;
+  st = device_check();
+  if (st != DSA_OK) return st;
+  return launch<true>(a, static_cast<hipStream_t>(stream));
+}
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported device or size";
+    case DSA_ERR_HIP: return "HIP runtime error";
+    case DSA_ERR_WORKSPACE: return "workspace too small for the chosen split";
+    default: return "unknown status";
+  }
+}
+
+int dsa_device_supported(int device) {
+  const DeviceInfo* d = device_info(device);
+  return d && d->gfx950 ? 1 : 0;
+}
+
+int dsa_version(void) { return 100; }
+
+}  // extern "C"

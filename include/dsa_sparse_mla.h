@@ -1,0 +1,163 @@
+/*
+ * dsa_sparse_mla.h -- C ABI of the DSA sparse MLA forward for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation: for each query token t and query head h, attention over only
+ * the KV rows that the token's index row names. One latent KV row per key is
+ * shared by every head (kv_group = 1). Rows are 576 bf16 wide (512 latent +
+ * 64 rope); scores use all 576 columns, values are the leading 512. The call
+ * returns the bf16 output O[t, h, 0:512] and the fp32 log-sum-exp LSE[t, h].
+ *
+ * Sources (pages on the web about this method):
+ *   - "[Feature] Add optional FlashMLA backend for DSA Sparse MLA"
+ *     (InternLM/xtuner PR 2083), sections Motivation and Runtime constraints:
+ *     the forward returns output and LSE; kv_group = 1; value width 512.
+ *   - "feat: add XTuner TileLang sparse MLA backend" (InternLM/lmdeploy PR
+ *     4904), section Performance > Isolated sparse MLA forward (bf16 Q/KV,
+ *     dqk 576, dv 512, topk 2048, 8 TP-local heads) and Validation (-1-padded
+ *     index rows); section Summary (packed prefill and zero-copy bf16
+ *     paged-cache decode run the same kernel) and the per-file overview
+ *     (logical-to-physical index mapping through the page table).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are plain device pointers. Strides are in elements; the last
+ *     dimension of q, kv, out is contiguous. bf16 pointers must be 16-byte
+ *     aligned and bf16 strides multiples of 8 elements; lse must be 4-byte
+ *     aligned.
+ *   - Ownership: every buffer belongs to the caller. The library allocates
+ *     nothing, keeps no pointer after it returns, and holds no state except a
+ *     per-device property cache filled once. Calls may come from several host
+ *     threads.
+ *   - Asynchrony: a call only enqueues kernels on `stream` (a hipStream_t;
+ *     NULL is the default stream). It never synchronises. Faults inside a
+ *     kernel surface at the caller's next synchronisation.
+ *   - Index entries are never checked on the host (that would need a sync).
+ *     The kernel skips an entry that names no row (-1 padding or any value
+ *     out of range), so no index value can make it read out of bounds.
+ *     Duplicate entries count once per occurrence.
+ *   - A token with no valid entry gets O = 0 and LSE = -inf.
+ *   - LSE is the natural log of sum_j exp(sm_scale * q . k_j).
+ *   - num_tokens == 0 is a no-op that returns DSA_OK.
+ *   - Each workgroup gathers at most 2048 index entries; a longer topk is split
+ *     over several workgroups whose partial results are merged by a second
+ *     kernel through the caller's workspace. Shorter rows may also be split
+ *     for parallelism (num_splits = 0 lets the library choose).
+ *   - Every entry point returns a dsa_status and never throws.
+ */
+#ifndef DSA_SPARSE_MLA_H
+#define DSA_SPARSE_MLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_DQK 576       /* query/key width: 512 latent + 64 rope */
+#define DSA_DV 512        /* value width: the latent part */
+#define DSA_MAX_HEADS 128
+#define DSA_MAX_TOPK 65536
+#define DSA_SEGMENT 2048  /* index entries one workgroup gathers */
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, stride or alignment */
+  DSA_ERR_UNSUPPORTED = 2,      /* device is not gfx950, or a size past the limits above */
+  DSA_ERR_HIP = 3,              /* a HIP runtime call or kernel launch failed */
+  DSA_ERR_WORKSPACE = 4         /* the chosen split needs more workspace than given */
+} dsa_status;
+
+/*
+ * Workspace query for dsa_sparse_mla_fwd / dsa_sparse_mla_fwd_paged.
+ *
+ * num_tokens, num_heads, topk: as in the forward call.
+ * num_splits: 0 = let the library choose; otherwise the split count the caller
+ *   will request. Must be >= ceil(topk / 2048) and <= topk.
+ * *splits_out (may be NULL): the split count a forward call with these
+ *   arguments uses, on the current device.
+ * *bytes_out: workspace bytes that call needs (0 when it does not split).
+ * Returns DSA_OK or DSA_ERR_INVALID_ARGUMENT / DSA_ERR_UNSUPPORTED.
+ */
+int dsa_sparse_mla_workspace_size(int64_t num_tokens, int32_t num_heads, int32_t topk,
+                                  int32_t num_splits, int32_t* splits_out,
+                                  int64_t* bytes_out);
+
+/*
+ * Sparse MLA forward over a flat KV array (packed or varlen prefill).
+ * Pages: xtuner PR 2083 (Motivation, Runtime constraints); lmdeploy PR 4904
+ * (Summary; Performance > Isolated sparse MLA forward; Validation).
+ *
+ * q        bf16 [num_tokens, num_heads, 576]; element (t,h,d) at
+ *          q + t*q_stride_tok + h*q_stride_head + d
+ * kv       bf16 [num_kv, 576]; row i at kv + i*kv_stride_row. Packed batches
+ *          use one array for all documents and global row ids in `indices`.
+ * indices  int32 [num_tokens, topk]; entry (t,j) at indices + t*idx_stride_tok + j.
+ *          A key iff 0 <= value < num_kv; anything else is skipped.
+ * sm_scale softmax scale applied to q . k.
+ * out      bf16 [num_tokens, num_heads, 512] (written), strides as for q.
+ * lse      fp32 [num_tokens, num_heads] (written); (t,h) at lse + t*lse_stride_tok + h.
+ * num_splits 0 = library's choice, else the split count (see the workspace query).
+ * workspace/workspace_bytes  device scratch of at least the queried size when
+ *          the call splits; may be NULL/0 otherwise. Its contents on entry do
+ *          not matter; calls that share one workspace must be stream-ordered.
+ * stream   hipStream_t to enqueue on.
+ *
+ * Limits: 1 <= num_heads <= 128, 1 <= topk <= 65536, num_kv * kv_stride_row * 2
+ * bytes < 64 GiB. out and lse must not overlap the inputs.
+ */
+int dsa_sparse_mla_fwd(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                       const void* kv, int64_t kv_stride_row, int64_t num_kv,
+                       const int32_t* indices, int64_t idx_stride_tok,
+                       int64_t num_tokens, int32_t num_heads, int32_t topk, float sm_scale,
+                       void* out, int64_t out_stride_tok, int64_t out_stride_head,
+                       float* lse, int64_t lse_stride_tok,
+                       int32_t num_splits, void* workspace, int64_t workspace_bytes,
+                       void* stream);
+
+/*
+ * Sparse MLA forward over a paged bf16 KV cache (decode), with no gather copy.
+ * Pages: lmdeploy PR 4904, Summary (zero-copy BF16 paged-cache decode with
+ * the same kernel) and the per-file overview (logical-to-physical index
+ * mapping); page size 64 in the decode workload.
+ *
+ * Query token t belongs to sequence b = t / q_per_seq; num_tokens = num_seqs * q_per_seq.
+ * kv_pages   bf16 [num_pages, page_size, 576]; row r of page p at
+ *            kv_pages + p*kv_stride_page + r*kv_stride_row.
+ * page_size  a power of two, 1..4096.
+ * page_table int32 [num_seqs, max_pages_per_seq]; (b,s) at page_table + b*page_table_stride + s.
+ * seq_lens   int32 [num_seqs]: tokens held in the cache for each sequence.
+ * indices    int32 [num_tokens, topk] logical positions p within the token's
+ *            sequence. p maps to row p % page_size of page
+ *            page_table[b, p / page_size]. The entry is skipped when p < 0,
+ *            p >= seq_lens[b], p / page_size >= max_pages_per_seq, or the
+ *            page id is outside [0, num_pages).
+ * Other arguments as in dsa_sparse_mla_fwd. Limits as there, with
+ * num_pages * kv_stride_page * 2 bytes < 64 GiB.
+ */
+int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                             const void* kv_pages, int64_t kv_stride_page, int64_t kv_stride_row,
+                             int64_t num_pages, int32_t page_size,
+                             const int32_t* page_table, int64_t page_table_stride,
+                             int32_t max_pages_per_seq, const int32_t* seq_lens,
+                             const int32_t* indices, int64_t idx_stride_tok,
+                             int32_t num_seqs, int32_t q_per_seq, int32_t num_heads,
+                             int32_t topk, float sm_scale,
+                             void* out, int64_t out_stride_tok, int64_t out_stride_head,
+                             float* lse, int64_t lse_stride_tok,
+                             int32_t num_splits, void* workspace, int64_t workspace_bytes,
+                             void* stream);
+
+/* Human-readable name of a dsa_status value (a static string). */
+const char* dsa_status_string(int status);
+
+/* 1 if HIP device `device` is a gfx950 (MI355X class) GPU, 0 if not or on error. */
+int dsa_device_supported(int device);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_SPARSE_MLA_H */

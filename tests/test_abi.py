@@ -1,0 +1,157 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and its host-side validation returns the documented status
+before any HIP call is made."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import dsa_sparse_mla_amd as dsa
+from dsa_sparse_mla_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa_sparse_mla.h")
+
+OK, INVALID, UNSUPPORTED, HIPERR, WORKSPACE = 0, 1, 2, 3, 4
+FAKE = 0x10000  # a 64 KiB-aligned non-null address; never dereferenced by the host checks
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = dsa.lib()
+    names = declared_functions()
+    assert "dsa_sparse_mla_fwd" in names and "dsa_sparse_mla_fwd_paged" in names
+    for name in names:
+        assert hasattr(L, name), f"missing export {name}"
+
+
+def test_single_hip_runtime_mapped():
+    import torch  # noqa: F401
+    dsa.lib()
+    maps = open("/proc/self/maps").read()
+    paths = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+    assert len(paths) == 1, paths
+
+
+def test_version_and_status_strings():
+    L = dsa.lib()
+    assert L.dsa_version() >= 100
+    for s in (OK, INVALID, UNSUPPORTED, HIPERR, WORKSPACE, 99):
+        assert isinstance(L.dsa_status_string(s), bytes)
+
+
+def _fwd(**over):
+    args = dict(q=FAKE, q_st=8 * 576, q_sh=576, kv=FAKE, kv_st=576, num_kv=100, idx=FAKE,
+                idx_st=2048, T=8, H=8, topk=2048, sm=0.04, out=FAKE, o_st=8 * 512, o_sh=512,
+                lse=FAKE, lse_st=8, splits=1, ws=None, ws_bytes=0, stream=None)
+    args.update(over)
+    return dsa.lib().dsa_sparse_mla_fwd(
+        args["q"], args["q_st"], args["q_sh"], args["kv"], args["kv_st"], args["num_kv"],
+        args["idx"], args["idx_st"], args["T"], args["H"], args["topk"], args["sm"],
+        args["out"], args["o_st"], args["o_sh"], args["lse"], args["lse_st"],
+        args["splits"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"T": 0}, OK),                                   # empty batch is a no-op
+    ({"T": -1}, INVALID),
+    ({"H": 0}, UNSUPPORTED),
+    ({"H": 129}, UNSUPPORTED),
+    ({"topk": 0}, UNSUPPORTED),
+    ({"topk": 65537}, UNSUPPORTED),
+    ({"q": None}, INVALID),
+    ({"kv": None}, INVALID),
+    ({"idx": None}, INVALID),
+    ({"out": None}, INVALID),
+    ({"lse": None}, INVALID),
+    ({"q": FAKE + 8}, INVALID),                       # q not 16-byte aligned
+    ({"kv": FAKE + 2}, INVALID),
+    ({"lse": FAKE + 2}, INVALID),
+    ({"q_sh": 577}, INVALID),                         # stride not a multiple of 8
+    ({"kv_st": 572}, INVALID),
+    ({"kv_st": 100}, INVALID),                        # rows overlap
+    ({"o_sh": 256}, INVALID),
+    ({"idx_st": 100}, INVALID),                       # rows shorter than topk
+    ({"num_kv": -1}, INVALID),
+    ({"sm": float("nan")}, INVALID),
+    ({"splits": -1}, INVALID),
+    ({"splits": 3000}, INVALID),                      # more splits than entries
+    ({"topk": 5000, "splits": 2}, INVALID),           # fewer than ceil(5000 / 2048)
+    ({"splits": 4}, WORKSPACE),                       # a split needs workspace
+    ({"splits": 4, "ws": FAKE, "ws_bytes": 100}, WORKSPACE),
+    ({"num_kv": 1 << 40}, UNSUPPORTED),               # offsets past 64 GiB
+])
+def test_fwd_host_validation(over, status):
+    assert _fwd(**over) == status
+
+
+def _paged(**over):
+    args = dict(q=FAKE, q_st=8 * 576, q_sh=576, kvp=FAKE, pst=64 * 576, rst=576, P=10, ps=64,
+                pt=FAKE, pt_st=16, maxp=16, sl=FAKE, idx=FAKE, idx_st=2048, S=4, Q=2, H=8,
+                topk=2048, sm=0.04, out=FAKE, o_st=8 * 512, o_sh=512, lse=FAKE, lse_st=8,
+                splits=1, ws=None, ws_bytes=0, stream=None)
+    args.update(over)
+    a = args
+    return dsa.lib().dsa_sparse_mla_fwd_paged(
+        a["q"], a["q_st"], a["q_sh"], a["kvp"], a["pst"], a["rst"], a["P"], a["ps"], a["pt"],
+        a["pt_st"], a["maxp"], a["sl"], a["idx"], a["idx_st"], a["S"], a["Q"], a["H"], a["topk"],
+        a["sm"], a["out"], a["o_st"], a["o_sh"], a["lse"], a["lse_st"], a["splits"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"S": 0}, OK),
+    ({"S": -1}, INVALID),
+    ({"Q": 0}, INVALID),
+    ({"ps": 48}, UNSUPPORTED),                        # not a power of two
+    ({"ps": 8192}, UNSUPPORTED),
+    ({"sl": None}, INVALID),
+    ({"pt": None}, INVALID),
+    ({"pt_st": 8}, INVALID),                          # table rows overlap
+    ({"pst": 63 * 576}, INVALID),                     # pages overlap
+    ({"kvp": None}, INVALID),
+    ({"rst": 576 + 4}, INVALID),
+    ({"H": 200}, UNSUPPORTED),
+    ({"P": 1 << 40}, UNSUPPORTED),
+])
+def test_paged_host_validation(over, status):
+    assert _paged(**over) == status
+
+
+def test_valid_call_reaches_the_device_check():
+    """A well-formed call passes validation; without a GPU the device check fails
+    with a HIP status (and nothing is launched). On a GPU machine this test is not
+    meaningful, so it only runs where no GPU is visible."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _fwd() in (HIPERR, UNSUPPORTED)
+
+
+@pytest.mark.parametrize("T,H,topk,req,splits,nbytes", [
+    (100, 8, 2048, 1, 1, 0),
+    (100, 8, 5000, 0, None, None),
+    (10, 64, 2048, 4, 4, 10 * 4 * 64 * 514 * 4),
+    (64, 8, 2048, 0, 1, 0),                           # small problems are not split
+])
+def test_workspace_query(T, H, topk, req, splits, nbytes):
+    s, b = binding.workspace_size(T, H, topk, req)
+    if splits is not None:
+        assert s == splits and b == nbytes
+    else:
+        assert s >= 3 and b == T * s * H * 514 * 4   # at least ceil(5000 / 2048) splits
+
+
+def test_workspace_query_rejects_bad_sizes():
+    with pytest.raises(binding.DsaError):
+        binding.workspace_size(10, 0, 2048, 0)
+    with pytest.raises(binding.DsaError):
+        binding.workspace_size(10, 8, 5000, 1)
