@@ -99,18 +99,21 @@ int device_check() {
   return d->gfx950 ? DSA_OK : DSA_ERR_UNSUPPORTED;
 }
 
+// Heads per workgroup: 16, 32 or 64 (HT head tiles of 16); more heads use
+// several workgroups per token, one per block of 64.
 template <bool PAGED>
-int launch(const dsa::FwdArgs& args, hipStream_t stream) {
+int launch(dsa::FwdArgs& args, hipStream_t stream) {
   const int H = args.num_heads;
-  const dim3 grid((unsigned)(args.num_tokens * args.splits));
-  if (H <= 16) {
-    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<1, 4, PAGED>), grid, dim3(256), 0, stream, args);
-  } else if (H <= 32) {
-    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<2, 2, PAGED>), grid, dim3(256), 0, stream, args);
-  } else if (H <= 64) {
-    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<4, 1, PAGED>), grid, dim3(256), 0, stream, args);
+  const int ht = H <= 16 ? 1 : H <= 32 ? 2 : 4;
+  args.head_blocks = (H + 16 * ht - 1) / (16 * ht);
+  const dim3 grid((unsigned)(args.num_tokens * args.splits * args.head_blocks));
+  const dim3 block(64 * dsa::kWaves);
+  if (ht == 1) {
+    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<1, PAGED>), grid, block, 0, stream, args);
+  } else if (ht == 2) {
+    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<2, PAGED>), grid, block, 0, stream, args);
   } else {
-    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<8, 1, PAGED>), grid, dim3(512), 0, stream, args);
+    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<4, PAGED>), grid, block, 0, stream, args);
   }
   if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
   if (args.splits > 1) {
