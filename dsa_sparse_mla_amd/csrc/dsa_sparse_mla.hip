@@ -129,7 +129,7 @@ int fill_outputs_and_splits(dsa::FwdArgs& a, const void* q, int64_t q_st, int64_
                             const int32_t* idx, int64_t idx_st, int64_t T, int32_t H, int32_t topk,
                             float sm_scale, void* out, int64_t o_st, int64_t o_sh, float* lse,
                             int64_t lse_st, int32_t num_splits, void* ws, int64_t ws_bytes) {
-  if (!std::isfinite(sm_scale)) return DSA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(sm_scale) || sm_scale < 0.f) return DSA_ERR_INVALID_ARGUMENT;
   int splits = 1, seg = topk;
   int64_t need = 0;
   int st = check_splits(T, H, topk, num_splits, &splits, &seg, &need);

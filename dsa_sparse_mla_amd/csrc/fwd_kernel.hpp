@@ -6,18 +6,23 @@
 //   1. index stage: read the token's index segment, keep the entries that name
 //      a KV row (for the paged cache: map logical position -> page -> row),
 //      and compact their row offsets, in order, into an LDS list;
-//   2. gather: stream the listed 576-wide bf16 rows, 64 keys per tile, from
+//   2. gather: stream the listed 576-wide bf16 rows, 32 keys per tile, from
 //      HBM straight into LDS (global_load_lds_dwordx4, 16 B per lane) through
-//      a two-stage ring, so the next tile is in flight while this one is used;
+//      a four-stage ring: two tiles are in flight while two are in use;
 //   3. S^T = K Q^T on bf16 MFMA (v_mfma_f32_16x16x32_bf16): 16 keys as M,
 //      16 heads as N, Q held in registers as the B operand;
-//   4. online softmax in fp32, base-2 domain (scale folded with log2 e);
-//   5. O^T += V^T P^T on bf16 MFMA (v_mfma_f32_16x16x32_bf16, 32 keys per
-//      step). The S^T accumulator layout is already the B-operand layout of
-//      P^T, so P never leaves registers. V is the leading 512 columns of the
-//      same LDS rows, read transposed with ds_read_b64_tr_b16;
+//   4. online softmax in fp32, base-2 domain (scale folded with log2 e),
+//      with a lazily moved reference max;
+//   5. O^T += V^T P^T on bf16 MFMA (v_mfma_f32_16x16x32_bf16, one 32-key
+//      step per tile). The S^T accumulator layout is already the B-operand
+//      layout of P^T, so P never leaves registers. V is the leading 512
+//      columns of the same LDS rows, read transposed with ds_read_b64_tr_b16;
 //   6. epilogue: normalise, write bf16 O and fp32 LSE -- or fp32 partials
 //      that a second kernel merges when the row was split.
+// Steps 3 and 5 are software-pipelined across tiles: the PV product of tile
+// j and the QK^T product of tile j+1 are independent, so one instruction
+// stream interleaves their MFMAs and LDS reads, and each hides the other's
+// latency.
 //
 // Work split: the workgroup's heads form HT tiles of 16. Wave w computes S
 // for head tile w % HT over every key of the tile, and PV for that head tile
@@ -25,13 +30,15 @@
 // one head tile repeat the (small) S product instead of exchanging P, so no
 // wave ever waits for another inside the key loop except at the tile barrier.
 //
-// LDS tile layout (64 keys, 72 KB): a latent region of 64 rows x 1 KB
-// (dims 0..511, i.e. V) and a rope region of 64 rows x 128 B (dims 512..575).
-// Granule G (16 B) of latent row r sits at position G ^ (r & 15), of rope row
-// r at G ^ ((r >> 1) & 7). Both spread the 16 rows of an MFMA operand read,
-// and the 16 rows of a transposed V read, over all 64 LDS banks, and both let
-// every per-lane LDS address be one of a few lane bases plus an immediate.
-// Each gather instruction fills exactly one latent row, or 8 rope rows.
+// LDS stage layout (32 keys, 36 KB): a latent region of 32 rows x 1 KB
+// (dims 0..511, i.e. V) and a rope region of 32 rows x 128 B (dims 512..575).
+// Granule G (16 B) of latent row r sits at position G ^ swz(r), with
+// swz(r) = (r & 15) ^ ((r & 1) << 3), and granule G of rope row r at
+// G ^ ((r >> 1) & 7). That spreads the 16 rows of an MFMA operand read over
+// all 64 LDS banks in each 16-lane quarter, and the rows of a transposed V
+// read over all banks in each 32-lane half, and it lets every per-lane LDS
+// address be one of a few lane bases plus an immediate. Each gather
+// instruction fills exactly one latent row, or 8 rope rows.
 //
 // Pages: "feat: add XTuner TileLang sparse MLA backend" (lmdeploy PR 4904),
 // Summary and Performance > Isolated sparse MLA forward; "[Feature] Add
@@ -46,20 +53,19 @@ namespace dsa {
 
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
-constexpr int kRowGran = 72;                          // 16-byte granules per 576-wide bf16 row
-constexpr int kTileKeys = 64;                         // keys per tile
-constexpr int kTileBytes = kTileKeys * kRowGran * 16;  // 73728
+constexpr int kTileKeys = 32;                         // keys per tile
+constexpr int kStages = 4;                            // LDS ring depth
+constexpr int kRopeOff = kTileKeys * 1024;            // rope region offset inside a stage
+constexpr int kStageBytes = kTileKeys * 1152;         // 36864
 constexpr int kWaves = 4;
-constexpr int kRopeOff = kTileKeys * 1024;            // rope region offset inside a tile
-constexpr int kDmaPerTile = kTileKeys * kRowGran / 64;  // 72 wave-wide 1 KB copies
-constexpr int kDmaPerWave = kDmaPerTile / kWaves;       // 18: 16 latent rows + 2 x 8 rope rows
+constexpr int kDmaPerWave = kTileKeys / kWaves + 1;   // 8 latent rows + 8 rope rows = 9 copies
 constexpr int kSegment = 2048;                        // index entries one workgroup compacts into LDS
 constexpr int kChunks = kSegment / 64;
 constexpr int kChunksPerWave = kChunks / kWaves;
-constexpr int kHeadsPerBlock = 64;                    // heads per workgroup at most
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kRescaleSlack = 8.f;                  // log2 units; p <= 256 between rescales
 
-static_assert(kDmaPerTile % kWaves == 0, "every wave issues the same number of copies");
+static_assert(kTileKeys == 8 * kWaves, "each wave copies 8 latent rows and 8 rope rows per tile");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -87,7 +93,7 @@ struct FwdArgs {
   int64_t num_tokens;
   int32_t num_heads;
   int32_t topk;
-  float scale_log2;        // sm_scale * log2(e)
+  float scale_log2;        // sm_scale * log2(e), >= 0
   uint16_t* out;           // bf16 [T, H, 512]
   int64_t o_st, o_sh;
   float* lse;              // fp32 [T, H]
@@ -107,6 +113,9 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
       (__attribute__((address_space(3))) const uint8_t*)(p)));
 }
 
+// Latent-row swizzle (see the layout note above).
+__host__ __device__ constexpr int swz(int r) { return (r & 15) ^ ((r & 1) << 3); }
+
 // One wave-wide 16-byte-per-lane copy HBM -> LDS: lane L's 16 bytes from
 // `src` land at LDS byte lds_base + 16 * L (lds_base is wave-uniform, in M0).
 // Issued through asm so the compiler does not tie every later LDS read to it;
@@ -116,8 +125,29 @@ __device__ __forceinline__ void dma_16b(const void* src, uint32_t lds_base) {
       "s_mov_b32 m0, %1\n\t"
       "global_load_lds_dwordx4 %0, off"
       :
-      : "v"(src), "s"(lds_base)
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
       : "memory");  // M0 is reserved by the compiler and not otherwise used by these kernels
+}
+
+// The same copy with a wave-uniform 64-bit base (SGPRs) and a per-lane
+// 32-bit byte offset.
+__device__ __forceinline__ void dma_16b_sbase(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations (the gather
+// copies) are still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else static_assert(N == 0, "unsupported count");
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -140,33 +170,17 @@ struct FwdShape {
   static constexpr int kDvParts = kWaves / HT;         // waves sharing one head tile
   static constexpr int kDvCols = kDv / kDvParts;       // value columns of one wave
   static constexpr int kDvTiles = kDvCols / 16;        // 16-column MFMA tiles of one wave
+  static constexpr int kSSteps = 2 * (kDqk / 32);      // QK^T MFMAs per tile (2 blocks x 18 chunks)
   static_assert(kWaves % HT == 0, "head tiles must divide the waves");
 };
 
-template <int HT, bool PAGED>
-__global__ void __launch_bounds__(256)
-sparse_mla_fwd_kernel(const FwdArgs a) {
-  using S = FwdShape<HT>;
-
-  __shared__ __attribute__((aligned(1024))) uint8_t s_stage[2 * kTileBytes];
-  __shared__ uint32_t s_goff[kSegment];
-  __shared__ int s_cnt[kChunks];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int hcol = lane & 15;   // MFMA row/column index of the lane
-  const int kq = lane >> 4;     // MFMA k-group of the lane
-
-  // Tokens in reverse order: in causal prefill the late tokens hold the most
-  // keys, and launching the longest rows first balances the tail.
-  const int64_t per_token = (int64_t)a.splits * a.head_blocks;
-  const int64_t bid = blockIdx.x;
-  const int64_t token = a.num_tokens - 1 - bid / per_token;
-  const int rem = (int)(bid % per_token);
-  const int split = rem / a.head_blocks;
-  const int hblock = rem % a.head_blocks;
-
-  // ---------------------------------------------------------------- 1. index stage
+// Index stage (step 1): keep the entries of this workgroup's segment that
+// name a KV row, and compact their row offsets (in 16-byte granules), in
+// order, into s_goff. The list is padded with offset 0 to a whole tile. All
+// waves of the workgroup call this; it returns the number of valid entries.
+template <bool PAGED>
+__device__ __forceinline__ int build_key_list(const FwdArgs& a, int64_t token, int split, int wave, int lane,
+                                              uint32_t* s_goff, int* s_cnt) {
   const int k0 = split * a.seg_len;
   const int n = min(a.topk - k0, a.seg_len);
   const int32_t* irow = a.idx + token * a.idx_st + k0;
@@ -220,14 +234,77 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
     const int y = __shfl_up(incl, d);
     if (lane >= d) incl += y;
   }
-  const int nvalid = __shfl(incl, kChunks - 1);
+  const int nvalid = __builtin_amdgcn_readfirstlane(__shfl(incl, kChunks - 1));   // uniform: scalar loop bounds
 #pragma unroll
   for (int c = 0; c < kChunksPerWave; ++c) {
     const int base = __shfl(incl - cnt, c * kWaves + wave);
     const uint64_t m = vmask[c];
     if ((m >> lane) & 1ull) s_goff[base + __popcll(m & ((1ull << lane) - 1ull))] = goff[c];
   }
+  // Pad the list to a whole tile with offset 0 (the first row; it exists
+  // whenever the list is not empty), so the gather needs no bounds check.
+  if (wave == 0 && nvalid + lane < ((nvalid + kTileKeys - 1) & ~(kTileKeys - 1))) s_goff[nvalid + lane] = 0;
   __syncthreads();
+
+  return nvalid;
+}
+
+// Gather (step 2) of tile j into LDS stage j % kStages: wave w copies latent
+// rows 8w .. 8w+7 (one 1 KB row per instruction; lane L fetches logical
+// granule L ^ swz(row)) and rope rows 8w .. 8w+7 (one instruction; lane L
+// fetches rope granule (L & 7) ^ ((row >> 1) & 7) of row 8w + L/8):
+// kDmaPerWave copies in all.
+__device__ __forceinline__ void issue_tile(const FwdArgs& a, const uint32_t* s_goff, uint32_t stage_lds, int j,
+                                           int wave, int lane) {
+  const uint32_t base = stage_lds + (j % kStages) * kStageBytes;
+  const uint4* gl = (const uint4*)(s_goff + j * kTileKeys + 8 * wave);
+  uint32_t go[8];
+#pragma unroll
+  for (int q2 = 0; q2 < 2; ++q2) {
+    const uint4 v = gl[q2];   // same address in every lane: a broadcast read
+    go[4 * q2 + 0] = v.x;
+    go[4 * q2 + 1] = v.y;
+    go[4 * q2 + 2] = v.z;
+    go[4 * q2 + 3] = v.w;
+  }
+  const int rrow = 8 * wave + (lane >> 3);
+  const uint32_t gr = s_goff[j * kTileKeys + rrow];
+  const uint32_t lane16 = (uint32_t)lane * 16u;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int row = 8 * wave + u;
+    const uint64_t sb = (uint64_t)a.kv + (uint64_t)__builtin_amdgcn_readfirstlane(go[u]) * 16ull;
+    dma_16b_sbase(sb, lane16 ^ (uint32_t)(swz(row) * 16), base + row * 1024);
+  }
+  const int g = (lane & 7) ^ ((rrow >> 1) & 7);
+  dma_16b(a.kv + ((uint64_t)gr + 64u + (uint32_t)g) * 16ull, base + kRopeOff + wave * 1024);
+}
+
+template <int HT, bool PAGED>
+__global__ void __launch_bounds__(256)
+sparse_mla_fwd_kernel(const FwdArgs a) {
+  using S = FwdShape<HT>;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t s_stage[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t s_goff[kSegment];
+  __shared__ int s_cnt[kChunks];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keep it scalar
+  const int hcol = lane & 15;   // MFMA row/column index of the lane
+  const int kq = lane >> 4;     // MFMA k-group of the lane
+
+  // Tokens in reverse order: in causal prefill the late tokens hold the most
+  // keys, and launching the longest rows first balances the tail.
+  const int64_t per_token = (int64_t)a.splits * a.head_blocks;
+  const int64_t bid = blockIdx.x;
+  const int64_t token = a.num_tokens - 1 - bid / per_token;
+  const int rem = (int)(bid % per_token);
+  const int split = rem / a.head_blocks;
+  const int hblock = rem % a.head_blocks;
+
+  // ---------------------------------------------------------------- 1. index stage
+  const int nvalid = build_key_list<PAGED>(a, token, split, wave, lane, s_goff, s_cnt);
 
   // ---------------------------------------------------------------- per-wave state
   const int ht = wave % HT;                  // head tile of this wave
@@ -247,178 +324,220 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
     }
     // Use Q once here, so the compiler's wait for these loads sits before the
     // loop; a wait at the first use inside the loop would also wait for the
-    // prefetch of the next tile on every iteration.
+    // gather of later tiles on every iteration.
 #pragma unroll
     for (int c = 0; c < kDqk / 32; ++c) asm volatile("" ::"v"(qreg[c]));
   }
 
   float4_t oacc[S::kDvTiles];
 #pragma unroll
-  for (int j = 0; j < S::kDvTiles; ++j) oacc[j] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max of this lane's head, log2 units
+  for (int j = 0; j < S::kDvTiles; ++j) {
+    oacc[j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    asm volatile("" : "+a"(oacc[j]));   // the accumulator lives in AGPRs throughout
+  }
+  float m_run = -INFINITY;  // reference max of this lane's head, log2 units
   float l_run = 0.f;        // running sum over the keys this lane holds
 
   // ---------------------------------------------------------------- 2. gather
   const int ntiles = (nvalid + kTileKeys - 1) / kTileKeys;
   const uint32_t stage_lds = lds_offset(s_stage);
-  // Gather of tile j: wave w copies latent rows 16w .. 16w+15 (one row, 1 KB,
-  // per instruction; lane L fetches logical granule L ^ (row & 15)) and rope
-  // rows 16w .. 16w+15 (8 rows per instruction; lane L fetches rope granule
-  // (L & 7) ^ ((row >> 1) & 7) of row 16w + 8t + L/8). Rows past the list
-  // re-read a valid row; nothing reads them back.
-  auto issue_tile = [&](int j) {
-    const uint32_t base = stage_lds + (j & 1) * kTileBytes;
-    uint32_t go[18];   // row offsets first: one LDS wait for the whole burst
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int key = j * kTileKeys + 16 * wave + u;
-      go[u] = s_goff[key < nvalid ? key : 0];
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int key = j * kTileKeys + 16 * wave + 8 * t + (lane >> 3);
-      go[16 + t] = s_goff[key < nvalid ? key : 0];
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int row = 16 * wave + u;
-      const uint8_t* src = a.kv + ((uint64_t)go[u] + (uint32_t)(lane ^ u)) * 16ull;  // row & 15 == u
-      dma_16b(src, __builtin_amdgcn_readfirstlane(base + row * 1024));
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int row = 16 * wave + 8 * t + (lane >> 3);
-      const int g = (lane & 7) ^ ((row >> 1) & 7);
-      const uint8_t* src = a.kv + ((uint64_t)go[16 + t] + 64u + (uint32_t)g) * 16ull;
-      dma_16b(src, __builtin_amdgcn_readfirstlane(base + kRopeOff + (2 * wave + t) * 1024));
-    }
-  };
-
-  // Per-lane LDS bases (inside a tile); every operand address is one of them
+  // Per-lane LDS bases (inside a stage); every operand address is one of them
   // plus a compile-time offset.
   // S operand, dims 32c + 8kq .. +7 of row 16b + hcol. Latent (c < 16):
-  // granule (4c + kq) ^ hcol = 4 * ((c & ~3) + ((c & 3) ^ (hcol >> 2))) + (kq ^ (hcol & 3)).
+  // granule (4c + kq) ^ fh = 4 * ((c & ~3) + ((c & 3) ^ (fh >> 2))) + (kq ^ (fh & 3)),
+  // fh = swz(hcol) = swz(16b + hcol).
+  const int fh = swz(hcol);
   int kbase[4];
 #pragma unroll
   for (int cl = 0; cl < 4; ++cl)
-    kbase[cl] = hcol * 1024 + 16 * (4 * (cl ^ (hcol >> 2)) + (kq ^ (hcol & 3)));
+    kbase[cl] = hcol * 1024 + 16 * (4 * (cl ^ (fh >> 2)) + (kq ^ (fh & 3)));
   // rope (c = 16, 17): granule (4(c-16) + kq) ^ ((hcol >> 1) & 7) of a 128 B row
   int rbase[2];
 #pragma unroll
   for (int cr = 0; cr < 2; ++cr) rbase[cr] = kRopeOff + hcol * 128 + 16 * ((4 * cr + kq) ^ ((hcol >> 1) & 7));
-  // V operand (transposed): row 32s2 + 16h + vr, columns dv0 + 16jt + 4(hcol & 3) .. +3,
-  // i.e. granule dv0/8 + 2jt + ((hcol >> 1) & 1) at byte (hcol & 1) * 8; rows have
-  // row & 15 == vr, so the stored granule is dv0/8 + 16(jt >> 3) + ((2(jt & 7) + gl) ^ vr).
+  // V operand (transposed): rows vr (slots 0-3) and 16 + vr (slots 4-7),
+  // columns dv0 + 16jt + 4(hcol & 3) .. +3, i.e. granule
+  // dv0/8 + 2jt + ((hcol >> 1) & 1) at byte (hcol & 1) * 8; both rows have
+  // swizzle swz(vr), so the stored granule is
+  // dv0/8 + 16(jt >> 3) + ((2(jt & 7) + gl) ^ swz(vr)).
   const int vr = 4 * kq + (hcol >> 2);
+  const int fv = swz(vr);
   int vbase[8];
 #pragma unroll
   for (int jl = 0; jl < 8; ++jl)
-    vbase[jl] = vr * 1024 + 16 * ((2 * jl + ((hcol >> 1) & 1)) ^ vr) + (hcol & 1) * 8 + 2 * dv0;
+    vbase[jl] = vr * 1024 + 16 * ((2 * jl + ((hcol >> 1) & 1)) ^ fv) + (hcol & 1) * 8 + 2 * dv0;
 
-  if (ntiles > 0) issue_tile(0);
-  for (int j = 0; j < ntiles; ++j) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 1 < ntiles) issue_tile(j + 1);
-    const uint8_t* tile = s_stage + (j & 1) * kTileBytes;
+  auto kread = [&](const uint8_t* st, int c, int b) {
+    const int off = c < 16 ? kbase[c & 3] + 64 * (c & ~3) + b * 16 * 1024 : rbase[c - 16] + b * 16 * 128;
+    return *(const bf16x8_t*)(st + off);
+  };
+  auto vread = [&](const uint8_t* st, int jt) {
+    const uint8_t* p = st + vbase[jt & 7] + 256 * (jt >> 3);
+    const short4_t lo = lds_read_tr16(p);               // keys vr      (block 0): slots 0-3
+    const short4_t hi = lds_read_tr16(p + 16 * 1024);   // keys 16 + vr (block 1): slots 4-7
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
-    // -------------------------------------------------------------- 3. S^T = K Q^T
-    // 4 independent accumulators (16-key blocks b); operands for dim chunk c+2
-    // are read while chunk c multiplies. The scheduling barriers keep the
-    // compiler from hoisting all 72 reads (and 288 registers) to the top.
-    float4_t sacc[4];
+  // ---------------------------------------------------------------- 3-5. pipelined steps
+  // One step runs, in one instruction stream:
+  //   phase A: the 36 QK^T MFMAs of tile jn (into sacc), interleaved 2:1 with
+  //            the first half of the PV MFMAs of the previous tile (operand
+  //            pk_cur), plus the gather issue of a later tile;
+  //   phase B: the rest of the PV MFMAs, each followed by one slice of the
+  //            online softmax of tile jn (which needs only sacc), so the VALU
+  //            work runs while the MFMA pipe is busy.
+  // The softmax writes P^T of tile jn to pk_next; moving the reference max
+  // only sets alpha, and the accumulator is rescaled after the step's last PV
+  // MFMA (O of the previous tile must be complete first).
+  float4_t sacc[2];
+  bf16x8_t pk_cur = {}, pk_next = {};
+  float sp[2][4];
+  float smx = -INFINITY;
+  float alpha = 1.f;
+
+  // Slice k of the softmax of tile jn. sacc[b][i] = raw score q . k of key
+  // 32jn + 16b + 4kq + i for head `head`; the scale (>= 0, folded with
+  // log2 e) is applied inside the exponent.
+  auto soft_piece = [&](int k, int jn) {
+    if (k == 0) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) sacc[b] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    auto kread = [&](int c, int b) {
-      const int off = c < 16 ? kbase[c & 3] + 64 * (c & ~3) + b * 16 * 1024 : rbase[c - 16] + b * 16 * 128;
-      return *(const bf16x8_t*)(tile + off);
-    };
-    bf16x8_t kring[2][4];
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) kring[0][b] = kread(0, b);
+        for (int i = 0; i < 4; ++i) sp[b][i] = sacc[b][i];
+      if ((jn + 1) * kTileKeys > nvalid) {   // the last tile: mask keys past the list
+        const int kb = jn * kTileKeys + 4 * kq;
 #pragma unroll
-    for (int c = 0; c < kDqk / 32; ++c) {
-      if (c + 1 < kDqk / 32) {
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) kring[(c + 1) & 1][b] = kread(c + 1, b);
+          for (int i = 0; i < 4; ++i)
+            if (kb + 16 * b + i >= nvalid) sp[b][i] = -INFINITY;
       }
+      smx = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kring[c & 1][b], qreg[c], sacc[b], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // -------------------------------------------------------------- 4. online softmax
-    // sacc[b][i] = score of key 64j + 16b + 4kq + i for head `head`
-    float p[4][4];
-    float mx = -INFINITY;
-    const int kbase = j * kTileKeys + 4 * kq;
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+        for (int i = 0; i < 4; ++i) smx = fmaxf(smx, sp[b][i]);
+    } else if (k == 1) {
+      smx = fmaxf(smx, __shfl_xor(smx, 16));
+    } else if (k == 2) {
+      smx = fmaxf(smx, __shfl_xor(smx, 32)) * a.scale_log2;
+      // Lazy rescaling: the reference max moves only when the tile max
+      // exceeds it by more than kRescaleSlack (log2 units); until then
+      // p = 2^(s - m_run) <= 2^kRescaleSlack. alpha = 1 unless it moves.
+      const float m_new = smx > m_run + kRescaleSlack ? fmaxf(m_run, smx) : m_run;   // finite: the tile holds a valid key
+      alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+    } else if (k == 3 || k == 4) {
+      const int b = k - 3;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = kbase + 16 * b + i < nvalid;
-        p[b][i] = ok ? sacc[b][i] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, p[b][i]);
+        sp[b][i] = fast_exp2(__builtin_fmaf(sp[b][i], a.scale_log2, -m_run));
+        l_run += sp[b][i];
       }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);   // finite: the tile holds a valid key
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[b][i] = fast_exp2(p[b][i] - m_new);
-        psum += p[b][i];
-      }
-    }
-    l_run = l_run * alpha + psum;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int jt = 0; jt < S::kDvTiles; ++jt) oacc[jt] *= alpha;
-    }
-    // P^T as the B operand of a 32-key step: slots 0-3 = block 2s, 4-7 = block 2s+1
-    bf16x8_t pk[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
+    } else {
+      // P^T as the B operand of the tile's 32-key step: slots 0-3 = block 0, 4-7 = block 1
       uint4 w;
-      w.x = pack_bf16x2(p[2 * s2][0], p[2 * s2][1]);
-      w.y = pack_bf16x2(p[2 * s2][2], p[2 * s2][3]);
-      w.z = pack_bf16x2(p[2 * s2 + 1][0], p[2 * s2 + 1][1]);
-      w.w = pack_bf16x2(p[2 * s2 + 1][2], p[2 * s2 + 1][3]);
-      pk[s2] = __builtin_bit_cast(bf16x8_t, w);
+      w.x = pack_bf16x2(sp[0][0], sp[0][1]);
+      w.y = pack_bf16x2(sp[0][2], sp[0][3]);
+      w.z = pack_bf16x2(sp[1][0], sp[1][1]);
+      w.w = pack_bf16x2(sp[1][2], sp[1][3]);
+      pk_next = __builtin_bit_cast(bf16x8_t, w);
+      // anchor the softmax here, beside the PV MFMAs (no sinking past the rescale)
+      asm volatile("" : "+v"(pk_next), "+v"(l_run));
     }
+  };
 
-    // -------------------------------------------------------------- 5. O^T += V^T P^T
-    // A operand of step s2 for value tile jt: column dv0 + 16jt + hcol of the
-    // 4 rows 32s2 + 4kq .. +3 (slots 0-3) and of the 4 rows 16 further (4-7),
-    // read transposed; operands for tile jt+2 are read while jt multiplies.
-    auto vread = [&](int jt, int s2) {
-      const uint8_t* p = tile + vbase[jt & 7] + 256 * (jt >> 3) + 32 * s2 * 1024;
-      const short4_t lo = lds_read_tr16(p);               // rows 32s2 + vr: slots 0-3
-      const short4_t hi = lds_read_tr16(p + 16 * 1024);   // rows 32s2 + 16 + vr: slots 4-7
-      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    bf16x8_t vring[3][2];
+  auto step = [&](const uint8_t* st_s, bool do_s, int jn, const uint8_t* st_pv, bool do_pv, int issue_j) {
+    constexpr int kS = S::kSSteps;        // 36 QK^T MFMAs: (chunk t/2, block t%2)
+    constexpr int kP = S::kDvTiles;       // PV MFMAs: value tile u
+    constexpr int kPA = kP / 2;           // PV MFMAs placed in phase A
+    constexpr int kKA = 4, kVA = 3;       // read-ahead (<= 15 LDS operations in flight)
+    constexpr int kPieces = 6;
+    bf16x8_t kr[kKA + 1], vrg[kVA + 1];
+    if (do_pv) {
 #pragma unroll
-    for (int jt = 0; jt < 2 && jt < S::kDvTiles; ++jt)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) vring[jt][s2] = vread(jt, s2);
-#pragma unroll
-    for (int jt = 0; jt < S::kDvTiles; ++jt) {
-      if (jt + 2 < S::kDvTiles) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) vring[(jt + 2) % 3][s2] = vread(jt + 2, s2);
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        oacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vring[jt % 3][s2], pk[s2], oacc[jt], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int u = 0; u < kVA; ++u) vrg[u] = vread(st_pv, u);
     }
+    auto pv_mfma = [&](int u) {
+      if (u + kVA < kP) vrg[(u + kVA) % (kVA + 1)] = vread(st_pv, u + kVA);
+      oacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vrg[u % (kVA + 1)], pk_cur, oacc[u], 0, 0, 0);
+    };
+    if (do_s) {
+      sacc[0] = sacc[1] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < kKA; ++t) kr[t] = kread(st_s, t >> 1, t & 1);
+      // phase A
+#pragma unroll
+      for (int t = 0; t < kS; ++t) {
+        if (t + kKA < kS) kr[(t + kKA) % (kKA + 1)] = kread(st_s, (t + kKA) >> 1, (t + kKA) & 1);
+        sacc[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[t % (kKA + 1)], qreg[t >> 1], sacc[t & 1], 0, 0, 0);
+        if (t >= kS - 2) asm volatile("" : "+v"(sacc[t & 1]));   // scores in VGPRs: read by the softmax
+        if (do_pv && (t & 1) && (t >> 1) < kPA) pv_mfma(t >> 1);
+        if (t == 3 && issue_j >= 0) issue_tile(a, s_goff, stage_lds, issue_j, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // phase B: remaining PV MFMAs with softmax slices (slot 0 left free so
+      // the last QK^T MFMA can finish); slices go to slots 1 .. nB-1
+      constexpr int kB = kP - kPA;
+#pragma unroll
+      for (int s2 = 0; s2 < kB; ++s2) {
+        if (do_pv) pv_mfma(kPA + s2);
+#pragma unroll
+        for (int k = 0; k < kPieces; ++k)
+          if (1 + k * (kB - 1) / kPieces == s2 || (kB == 1 && s2 == 0)) soft_piece(k, jn);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if (do_pv) {
+#pragma unroll
+      for (int u = 0; u < kP; ++u) {
+        pv_mfma(u);
+        if (u == 1 && issue_j >= 0) issue_tile(a, s_goff, stage_lds, issue_j, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // keep the loop-carried accumulator in AGPRs (no copies between tiles)
+#pragma unroll
+    for (int jt = 0; jt < kP; ++jt) asm volatile("" : "+a"(oacc[jt]));
+    if (do_s) {
+      if (__ballot(alpha != 1.f)) {   // the reference moved: rescale O (rare)
+#pragma unroll
+        for (int jt = 0; jt < kP; ++jt) {
+          // The accumulator lives in AGPRs (it is only ever an MFMA operand);
+          // copy it to VGPRs here, scale, and put it back, so that the copies
+          // stay inside this rarely taken branch.
+          float4_t t = oacc[jt];
+          asm volatile("" : "+v"(t));
+          t *= alpha;
+          asm volatile("" : "+a"(t));
+          oacc[jt] = t;
+        }
+      }
+      pk_cur = pk_next;
+    }
+  };
+
+  auto stage_ptr = [&](int j) { return (const uint8_t*)s_stage + (j % kStages) * kStageBytes; };
+
+  if (ntiles > 0) {
+    // prologue: tiles 0..2 in flight, then QK^T and softmax of tile 0
+    issue_tile(a, s_goff, stage_lds, 0, wave, lane);
+    if (ntiles > 1) issue_tile(a, s_goff, stage_lds, 1, wave, lane);
+    if (ntiles > 2) issue_tile(a, s_goff, stage_lds, 2, wave, lane);
+    if (ntiles > 2) wait_vmem<2 * kDmaPerWave>();
+    else if (ntiles > 1) wait_vmem<kDmaPerWave>();
+    else wait_vmem<0>();
+    __syncthreads();
+    step(stage_ptr(0), true, 0, stage_ptr(0), false, -1);
+    // steady state: PV of tile j with QK^T and softmax of tile j+1
+    for (int j = 0; j + 1 < ntiles; ++j) {
+      if (j + 2 < ntiles) wait_vmem<kDmaPerWave>();   // tile j+1 landed; tile j+2 may still fly
+      else wait_vmem<0>();
+      __syncthreads();   // ... in every wave; and tile j-1's stage is free for tile j+3
+      step(stage_ptr(j + 1), true, j + 1, stage_ptr(j), true, j + 3 < ntiles ? j + 3 : -1);
+    }
+    // PV of the last tile
+    step(stage_ptr(ntiles - 1), false, ntiles - 1, stage_ptr(ntiles - 1), true, -1);
   }
 
   // ---------------------------------------------------------------- 6. epilogue

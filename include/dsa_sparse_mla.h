@@ -93,7 +93,8 @@ int dsa_sparse_mla_workspace_size(int64_t num_tokens, int32_t num_heads, int32_t
  *          use one array for all documents and global row ids in `indices`.
  * indices  int32 [num_tokens, topk]; entry (t,j) at indices + t*idx_stride_tok + j.
  *          A key iff 0 <= value < num_kv; anything else is skipped.
- * sm_scale softmax scale applied to q . k.
+ * sm_scale softmax scale applied to q . k; finite and >= 0 (the kernels
+ *          fold it into the exponent after taking the raw-score max).
  * out      bf16 [num_tokens, num_heads, 512] (written), strides as for q.
  * lse      fp32 [num_tokens, num_heads] (written); (t,h) at lse + t*lse_stride_tok + h.
  * num_splits 0 = library's choice, else the split count (see the workspace query).

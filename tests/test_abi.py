@@ -82,6 +82,8 @@ def _fwd(**over):
     ({"idx_st": 100}, INVALID),                       # rows shorter than topk
     ({"num_kv": -1}, INVALID),
     ({"sm": float("nan")}, INVALID),
+    ({"sm": float("inf")}, INVALID),
+    ({"sm": -0.04}, INVALID),                         # the score max is taken before scaling
     ({"splits": -1}, INVALID),
     ({"splits": 3000}, INVALID),                      # more splits than entries
     ({"topk": 5000, "splits": 2}, INVALID),           # fewer than ceil(5000 / 2048)

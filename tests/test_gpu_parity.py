@@ -194,6 +194,19 @@ def test_peaky_scores_stay_finite():
     check(np32(out), np32(lse), *ref_flat(q, kv, idx, 1 / 24), "peaky")
 
 
+@pytest.mark.parametrize("sm", [0.0, 1e-4, 0.5])
+def test_softmax_scale_range(sm):
+    """sm_scale = 0 gives uniform weights (O = mean of the latent rows, LSE =
+    log of the key count); a large scale makes every row nearly one-hot."""
+    q, kv, idx = random_case(T=40, H=16, N=3000, topk=700, seed=13)
+    out, lse = run_flat(q, kv, idx, sm)
+    ro, rl = ref_flat(q, kv, idx, sm)
+    check(np32(out), np32(lse), ro, rl, f"scale{sm}")
+    if sm == 0.0:
+        n = ((idx >= 0) & (idx < 3000)).sum(1).numpy()
+        np.testing.assert_allclose(np32(lse), np.log(n)[:, None].repeat(16, 1), rtol=1e-6, atol=1e-6)
+
+
 def test_strided_inputs_and_outputs():
     T, H, N, k = 12, 8, 700, 200
     q_big, kv, idx = random_case(T=T, H=H * 2, N=N, topk=k, seed=13)
