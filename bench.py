@@ -57,6 +57,62 @@ def traffic_for(workload: str):
     return rec.get("bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20   # the calibration copy reads and writes this many bytes
+
+
+def copy_calibration(dev, reps: int = 3):
+    """Launch a plain elementwise copy of known size (read COPY_BYTES, write
+    COPY_BYTES) so that counter runs can scale FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: str):
+    """Turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE, in
+    KiB per dispatch) into HBM bytes per forward launch, each scaled by what
+    the same counter reads for the calibration copy, and store the result
+    under profiles/ with the kernel-source hash it was taken on."""
+    import csv
+    import statistics
+
+    def per_dispatch(path, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (row["Dispatch_Id"], row["Kernel_Name"])
+                vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+        return vals
+
+    out = {"workload": workload, "source_hash": source_hash(), "command": command}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = per_dispatch(path, counter)
+        copy = [v for (d, k), v in vals.items() if "neg" in k]
+        fwd = [v for (d, k), v in vals.items() if "sparse_mla_fwd_kernel" in k]
+        if not copy or not fwd:
+            raise SystemExit(f"{path}: no calibration copy or forward dispatch with {counter}")
+        factor = COPY_BYTES / (statistics.median(copy) * 1024.0)
+        fwd_bytes = statistics.median(fwd) * 1024.0 * factor
+        tag = counter.split("_")[0].lower()
+        out[f"{tag}_kib_copy"] = statistics.median(copy)
+        out[f"{tag}_kib_fwd"] = statistics.median(fwd)
+        out[f"{tag}_factor"] = round(factor, 4)
+        out[f"{tag}_bytes"] = round(fwd_bytes)
+        out[f"{tag}_dispatches"] = len(fwd)
+    out["bytes_per_launch"] = out["fetch_bytes"] + out["write_bytes"]
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def valid_keys(d) -> int:
     import torch
     if "kv" in d:
@@ -134,7 +190,17 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 skips it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a copy of known size (for HBM counter scaling)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: store HBM bytes per launch from two counter runs")
+    ap.add_argument("--traffic-command", default="",
+                    help="the profiling command, recorded with --summarize-traffic")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        summarize_traffic(args.workload, *args.summarize_traffic, args.traffic_command)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -176,6 +242,8 @@ def main():
                                      d["indices"], d["sm_scale"], d["q_per_seq"], out=out, lse=lse,
                                      num_splits=args.num_splits, workspace=ws)
 
+    if args.copy_calibration:
+        copy_calibration(dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -431,10 +431,15 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
     } else if (k == 3 || k == 4) {
       const int b = k - 3;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sp[b][i] = fast_exp2(__builtin_fmaf(sp[b][i], a.scale_log2, -m_run));
-        l_run += sp[b][i];
+      for (int i = 0; i < 4; ++i) sp[b][i] = fast_exp2(__builtin_fmaf(sp[b][i], a.scale_log2, -m_run));
+      if ((jn + 1) * kTileKeys > nvalid) {   // last tile: a masked slot has weight 0 (also when the scale is 0)
+        const int kb = jn * kTileKeys + 4 * kq + 16 * b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kb + i >= nvalid) sp[b][i] = 0.f;
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l_run += sp[b][i];
     } else {
       // P^T as the B operand of the tile's 32-key step: slots 0-3 = block 0, 4-7 = block 1
       uint4 w;
