@@ -144,16 +144,15 @@ __device__ __forceinline__ void dma_16b_sbase(uint64_t sbase, uint32_t voff, uin
 // copies) are still outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-  else static_assert(N == 0, "unsupported count");
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+// Two floats to bf16 (round to nearest even), lo in the low half: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;  // round to nearest even
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){lo, hi}, bf16x2_t));
 }
 
 // Transposed read: with lane j of each 16-lane group pointing at 4 bf16 of
@@ -163,7 +162,6 @@ __device__ __forceinline__ short4_t lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(
       (__attribute__((address_space(3))) uint8_t*)(p)));
 }
-
 template <int HT>
 struct FwdShape {
   static constexpr int kHeads = 16 * HT;               // heads of the workgroup
@@ -250,10 +248,10 @@ __device__ __forceinline__ int build_key_list(const FwdArgs& a, int64_t token, i
 }
 
 // Gather (step 2) of tile j into LDS stage j % kStages: wave w copies latent
-// rows 8w .. 8w+7 (one 1 KB row per instruction; lane L fetches logical
-// granule L ^ swz(row)) and rope rows 8w .. 8w+7 (one instruction; lane L
-// fetches rope granule (L & 7) ^ ((row >> 1) & 7) of row 8w + L/8):
-// kDmaPerWave copies in all.
+// rows 8w .. 8w+7 (one 1 KB row per instruction; lane i fetches logical
+// granule i ^ swz(row)) and rope rows
+// 8w .. 8w+7 (one instruction; lane i fetches rope granule
+// (i & 7) ^ ((row >> 1) & 7) of row 8w + i/8): kDmaPerWave copies in all.
 __device__ __forceinline__ void issue_tile(const FwdArgs& a, const uint32_t* s_goff, uint32_t stage_lds, int j,
                                            int wave, int lane) {
   const uint32_t base = stage_lds + (j % kStages) * kStageBytes;
