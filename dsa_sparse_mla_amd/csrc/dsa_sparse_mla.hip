@@ -13,6 +13,7 @@
 
 #include "dsa_sparse_mla.h"
 #include "fwd_kernel.hpp"
+#include "fwd_kernel_ws.hpp"
 
 namespace {
 
@@ -51,12 +52,21 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // Split choice. Each workgroup gathers at most kSegment entries. With few
 // tokens and long rows, more workgroups per token fill the 256 CUs; short
 // problems are not split (the merge pass would cost more than it saves).
-int choose_splits(int64_t T, int32_t topk, int32_t requested, int cus) {
+// Head tiles of 16 per workgroup (HT) and workgroups per token along the heads.
+int head_tiles(int32_t H) { return H <= 16 ? 1 : H <= 32 ? 2 : 4; }
+int head_blocks(int32_t H) { return (H + 16 * head_tiles(H) - 1) / (16 * head_tiles(H)); }
+
+// Splits of each index row: at least ceil(topk / 2048); for a large enough
+// problem, doubled while the grid holds fewer than two workgroups per CU
+// (one workgroup fills a CU, and a second hides its start-up and tail) and
+// each split keeps at least 128 entries.
+int choose_splits(int64_t T, int32_t H, int32_t topk, int32_t requested, int cus) {
   const int smin = (topk + dsa::kSegment - 1) / dsa::kSegment;
   if (requested > 0) return requested;
   int s = smin;
   if (T * (int64_t)topk >= (int64_t)256 * 1024) {
-    while (T * s < 4LL * cus && (int64_t)s * 2 * 128 <= topk && s < 64) s *= 2;
+    const int64_t per_split = T * head_blocks(H);
+    while (per_split * s < 2LL * cus && (int64_t)s * 2 * 128 <= topk && s < 64) s *= 2;
   }
   return s;
 }
@@ -66,7 +76,7 @@ int check_splits(int64_t T, int32_t H, int32_t topk, int32_t requested, int* spl
   const int smin = (topk + dsa::kSegment - 1) / dsa::kSegment;
   if (requested < 0) return DSA_ERR_INVALID_ARGUMENT;
   if (requested > 0 && (requested < smin || requested > topk)) return DSA_ERR_INVALID_ARGUMENT;
-  const int s = choose_splits(T, topk, requested, requested > 0 ? 256 : current_device_cus());
+  const int s = choose_splits(T, H, topk, requested, requested > 0 ? 256 : current_device_cus());
   const int seg = (topk + s - 1) / s;  // <= kSegment because s >= smin; a split may own no entry
   *splits = s;
   *seg_len = seg;
@@ -104,8 +114,8 @@ int device_check() {
 template <bool PAGED>
 int launch(dsa::FwdArgs& args, hipStream_t stream) {
   const int H = args.num_heads;
-  const int ht = H <= 16 ? 1 : H <= 32 ? 2 : 4;
-  args.head_blocks = (H + 16 * ht - 1) / (16 * ht);
+  const int ht = head_tiles(H);
+  args.head_blocks = head_blocks(H);
   const dim3 grid((unsigned)(args.num_tokens * args.splits * args.head_blocks));
   const dim3 block(64 * dsa::kWaves);
   if (ht == 1) {
@@ -113,7 +123,7 @@ int launch(dsa::FwdArgs& args, hipStream_t stream) {
   } else if (ht == 2) {
     hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<2, PAGED>), grid, block, 0, stream, args);
   } else {
-    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<4, PAGED>), grid, block, 0, stream, args);
+    hipLaunchKernelGGL((dsa::sparse_mla_fwd_ws_kernel<PAGED>), grid, dim3(64 * dsa::kWsWaves), 0, stream, args);
   }
   if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
   if (args.splits > 1) {

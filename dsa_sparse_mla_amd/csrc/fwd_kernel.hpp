@@ -61,7 +61,6 @@ constexpr int kWaves = 4;
 constexpr int kDmaPerWave = kTileKeys / kWaves + 1;   // 8 latent rows + 8 rope rows = 9 copies
 constexpr int kSegment = 2048;                        // index entries one workgroup compacts into LDS
 constexpr int kChunks = kSegment / 64;
-constexpr int kChunksPerWave = kChunks / kWaves;
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kRescaleSlack = 8.f;                  // log2 units; p <= 256 between rescales
 
@@ -176,9 +175,12 @@ struct FwdShape {
 // name a KV row, and compact their row offsets (in 16-byte granules), in
 // order, into s_goff. The list is padded with offset 0 to a whole tile. All
 // waves of the workgroup call this; it returns the number of valid entries.
-template <bool PAGED>
+// NW waves share the work (chunk c of wave w covers entries (c NW + w) * 64 ..).
+template <bool PAGED, int NW = kWaves>
 __device__ __forceinline__ int build_key_list(const FwdArgs& a, int64_t token, int split, int wave, int lane,
                                               uint32_t* s_goff, int* s_cnt) {
+  constexpr int kChunksPerWave = kChunks / NW;
+  static_assert(kChunks % NW == 0, "chunks must divide over the waves");
   const int k0 = split * a.seg_len;
   const int n = min(a.topk - k0, a.seg_len);
   const int32_t* irow = a.idx + token * a.idx_st + k0;
@@ -186,7 +188,7 @@ __device__ __forceinline__ int build_key_list(const FwdArgs& a, int64_t token, i
   int32_t val[kChunksPerWave];
 #pragma unroll
   for (int c = 0; c < kChunksPerWave; ++c) {
-    const int e = (c * kWaves + wave) * 64 + lane;
+    const int e = (c * NW + wave) * 64 + lane;
     val[c] = e < n ? irow[e] : -1;
   }
   uint32_t goff[kChunksPerWave];
@@ -221,7 +223,7 @@ __device__ __forceinline__ int build_key_list(const FwdArgs& a, int64_t token, i
     int cnt = 0;
 #pragma unroll
     for (int c = 0; c < kChunksPerWave; ++c) cnt = lane == c ? __popcll(vmask[c]) : cnt;
-    s_cnt[lane * kWaves + wave] = cnt;
+    s_cnt[lane * NW + wave] = cnt;
   }
   __syncthreads();
   // exclusive prefix of the chunk counts, computed by every wave (lane c = chunk c)
@@ -235,7 +237,7 @@ __device__ __forceinline__ int build_key_list(const FwdArgs& a, int64_t token, i
   const int nvalid = __builtin_amdgcn_readfirstlane(__shfl(incl, kChunks - 1));   // uniform: scalar loop bounds
 #pragma unroll
   for (int c = 0; c < kChunksPerWave; ++c) {
-    const int base = __shfl(incl - cnt, c * kWaves + wave);
+    const int base = __shfl(incl - cnt, c * NW + wave);
     const uint64_t m = vmask[c];
     if ((m >> lane) & 1ull) s_goff[base + __popcll(m & ((1ull << lane) - 1ull))] = goff[c];
   }
