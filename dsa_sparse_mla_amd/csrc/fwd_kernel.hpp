@@ -176,9 +176,11 @@ struct FwdShape {
 // order, into s_goff. The list is padded with offset 0 to a whole tile. All
 // waves of the workgroup call this; it returns the number of valid entries.
 // NW waves share the work (chunk c of wave w covers entries (c NW + w) * 64 ..).
-template <bool PAGED, int NW = kWaves>
+// after_issue() runs once the index loads are issued and before their values
+// are used: loads issued there overlap the index latency.
+template <bool PAGED, int NW = kWaves, typename F>
 __device__ __forceinline__ int build_key_list(const FwdArgs& a, int64_t token, int split, int wave, int lane,
-                                              uint32_t* s_goff, int* s_cnt) {
+                                              uint32_t* s_goff, int* s_cnt, F&& after_issue) {
   constexpr int kChunksPerWave = kChunks / NW;
   static_assert(kChunks % NW == 0, "chunks must divide over the waves");
   const int k0 = split * a.seg_len;
@@ -191,6 +193,9 @@ __device__ __forceinline__ int build_key_list(const FwdArgs& a, int64_t token, i
     const int e = (c * NW + wave) * 64 + lane;
     val[c] = e < n ? irow[e] : -1;
   }
+  __builtin_amdgcn_sched_barrier(0);
+  after_issue();
+  __builtin_amdgcn_sched_barrier(0);
   uint32_t goff[kChunksPerWave];
   uint64_t vmask[kChunksPerWave];
   if constexpr (!PAGED) {
@@ -304,7 +309,7 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
   const int hblock = rem % a.head_blocks;
 
   // ---------------------------------------------------------------- 1. index stage
-  const int nvalid = build_key_list<PAGED>(a, token, split, wave, lane, s_goff, s_cnt);
+  const int nvalid = build_key_list<PAGED>(a, token, split, wave, lane, s_goff, s_cnt, [] {});
 
   // ---------------------------------------------------------------- per-wave state
   const int ht = wave % HT;                  // head tile of this wave

@@ -10,23 +10,33 @@
 //   S waves (w = 0..3): head half hh = w & 1, key block kd = (w >> 1) & 1.
 //     QK^T of 32 heads against keys 16kd .. 16kd+15 of a tile: 36 16x16x32
 //     MFMAs, two head tiles per K read, Q^T mostly in the accumulator file.
-//     Raw fp32 scores go to LDS. The S waves also issue the gather.
-//   PV waves (w = 4..7): head half hh, value half kd.
-//     The online softmax of all 32 keys of a tile for 32 heads: each lane
-//     reads the 16 scores that form its P^T operand. Then O^T[256 columns x
-//     32 heads] += V^T P^T: 16 32x32x16 MFMAs, O^T in the accumulator file.
-//     The two PV waves of a head half compute the same reference maxima from
-//     the same scores, so they scale P and O identically without talking.
+//     Then the softmax numerators of those scores: each exponential is taken
+//     once, by the wave that holds the score. They go to LDS as bf16 P.
+//   PV waves (w = 4..7): value quarter pw = w & 3, all 64 heads.
+//     O^T[128 columns x 64 heads] += V^T P^T: 16 32x32x16 MFMAs, each V^T
+//     operand used for two head tiles (every V element is read from LDS
+//     once), O^T in the accumulator file. The PV waves also issue the gather.
 // The hardware places wave w on SIMD w % 4, so each SIMD runs one S wave and
 // one PV wave. Per tile every SIMD has 36 x 16 + 16 x 32 = 1088 MFMA clocks.
 //
-// Pipeline: in iteration j the S waves score tile j+1 while the PV waves
-// finish tile j. One workgroup barrier per tile publishes the scores and the
-// gathered rows.
+// Reference maxima. P must use one reference per head across both key blocks
+// and all PV waves, and it must be known before the scores that it scales:
+// the S waves use the reference of the tiles before (lagged). A tile whose
+// scaled score exceeds its head's reference by more than kWsSlack (log2
+// units; always the case for the first tile) is settled in one extra step:
+// the S waves agree on new references from the published block maxima,
+// rewrite that tile's P, and publish the factors by which the PV waves
+// rescale O. Between such steps P <= 2^kWsSlack, far from the bf16 and fp32
+// ranges, and bf16 keeps its relative precision at any magnitude.
 //
-// LDS (exactly 160 KB): the 4-stage tile ring (kStages x 36 KB), plus two
-// score buffers of 8 KB (tile parity). During the index stage the first
-// holds the compacted key list and the second the chunk counts.
+// Pipeline: in iteration j the S waves settle tile j and score tile j+1,
+// while the PV waves accumulate tile j and gather tile j+3. One workgroup
+// barrier per tile publishes P, the flags and the gathered rows.
+//
+// LDS: the 4-stage tile ring (kStages x 36 KB), two P buffers of 4 KB (tile
+// parity), block maxima, flags, factors and row sums (157472 bytes in all).
+// During the index stage the P buffers hold the compacted key list and the
+// block maxima the chunk counts.
 //
 // Pages: "feat: add XTuner TileLang sparse MLA backend" (lmdeploy PR 4904),
 // Performance > Isolated sparse MLA forward (64-head operation of the other
@@ -41,8 +51,9 @@ namespace dsa {
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kWsWaves = 8;
-constexpr int kScoreBytes = 2 * 32 * 32 * 4;   // one tile: [hh 2][32 heads][32 keys] fp32
-static_assert(kScoreBytes == kSegment * 4, "a score buffer doubles as the key list");
+constexpr int kPBytes = 64 * kTileKeys * 2;   // P of one tile: [64 heads][32 keys] bf16
+static_assert(2 * kPBytes == kSegment * 4, "the two P buffers double as the key list");
+constexpr float kWsSlack = 16.f;              // log2 units: P <= 65536 between reference moves
 
 // Latent-row swizzle of this kernel's tiles: granule G of latent row r is
 // stored at G ^ swz_ws(r). A bijection of r & 15 (16 consecutive rows read at
@@ -50,10 +61,21 @@ static_assert(kScoreBytes == kSegment * 4, "a score buffer doubles as the key li
 // half-wave transposed V read also hit distinct banks.
 __host__ __device__ constexpr int swz_ws(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-// Score buffer: 16-byte group g (keys 4g .. 4g+3) of head h sits at group
-// g ^ ((h >> 1) & 7) of the head's 128-byte row, so that 16 consecutive heads
-// at one group use 16 distinct 4-bank groups.
-__host__ __device__ constexpr int score_off(int h, int g) { return h * 128 + 16 * (g ^ ((h >> 1) & 7)); }
+// Key rows of the QK^T operand. Lane i of a 16x16x32 MFMA operand supplies
+// row i & 15; the lane reading row i loads key 4 sigma(i >> 2) + (i & 3) of
+// its 16-key block, so output row 4q + e holds key 4 sigma(q) + e. The
+// permutation matters for LDS banks: a ds_read_b128 serves in one cycle the
+// 16 lanes of a half-wave whose quad index (lane bits 2..4) has one parity,
+// and with sigma = (2, 0, 1, 3) those lanes hit 16 distinct slots under
+// swz_ws (with the identity they pair up: a 2-way conflict on every K read).
+__host__ __device__ constexpr int key_sigma(int q) { return (0x3102 >> (4 * q)) & 15; }
+__host__ __device__ constexpr int key_rho(int i) { return 4 * key_sigma(i >> 2) + (i & 3); }
+
+// P buffer: the 16-byte group g (keys 8g .. 8g+7) of head h sits at group
+// g ^ ((h >> 2) & 3) of the head's 64-byte row. 16 consecutive heads at one
+// group then cover all 64 banks (PV operand reads), and so do the 8-byte
+// writes of 16 heads x 2 half-groups (S waves).
+__host__ __device__ constexpr int p_off(int h, int g) { return h * 64 + 16 * (g ^ ((h >> 2) & 3)); }
 
 __device__ __forceinline__ short4_t lds_tr16_at(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(uintptr_t)addr);
@@ -61,34 +83,43 @@ __device__ __forceinline__ short4_t lds_tr16_at(uint32_t addr) {
 __device__ __forceinline__ bf16x8_t lds_b128_at(uint32_t addr) {
   return *(__attribute__((address_space(3))) const bf16x8_t*)(uintptr_t)addr;
 }
-__device__ __forceinline__ float4_t lds_f4_at(uint32_t addr) {
-  return *(__attribute__((address_space(3))) const float4_t*)(uintptr_t)addr;
-}
-__device__ __forceinline__ void lds_f4_write_at(uint32_t addr, float4_t v) {
-  *(__attribute__((address_space(3))) float4_t*)(uintptr_t)addr = v;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void lds_write_b64_at(uint32_t addr, u32x2_t v) {
+  *(__attribute__((address_space(3))) u32x2_t*)(uintptr_t)addr = v;
 }
 
-// Combine over lanes l and l ^ 32 with the gfx950 lane swap (VALU, no LDS
-// round trip). The swap reads VGPRs that the previous VALU instruction may
-// have just written, so s_nop guards both sides of it.
+// Lane swaps of gfx950 (VALU, no LDS round trip): swap16 exchanges the odd
+// 16-lane rows of a with the even rows of b, swap32 the high half of a with
+// the low half of b. They read VGPRs that the previous VALU instruction may
+// have just written, so s_nop guards both sides.
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
 __device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
-__device__ __forceinline__ float max_halves(float x) {
+// max / sum over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48)
+__device__ __forceinline__ float max_kgroups(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-  swap32(a, b);   // a holds the low half's value in both halves, b the high half's
+  swap16(a, b);   // a: rows (0,0,2,2), b: rows (1,1,3,3)
+  x = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap32(a, b);   // a: halves (0,0), b: halves (1,1)
   return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
-__device__ __forceinline__ float sum_halves(float x) {
+__device__ __forceinline__ float sum_kgroups(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap16(a, b);
+  x = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+  a = __builtin_bit_cast(uint32_t, x), b = a;
   swap32(a, b);
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
-// Lazy reference (log2 units): it moves only when a tile maximum exceeds it
-// by more than kRescaleSlack, so O is rescaled rarely after the first tile.
+// New reference from the old one and a tile maximum (log2 units): it moves
+// only beyond the slack.
 __device__ __forceinline__ float next_ref(float m_run, float m_tile) {
-  return m_tile > m_run + kRescaleSlack ? fmaxf(m_run, m_tile) : m_run;
+  return m_tile > m_run + kWsSlack ? fmaxf(m_run, m_tile) : m_run;
 }
 __device__ __forceinline__ float ref_factor(float m_old, float m_new) {
   return m_new == m_old ? 1.f : fast_exp2(m_old - m_new);   // m_old = -inf gives 0
@@ -98,17 +129,19 @@ template <bool PAGED>
 __global__ void __launch_bounds__(64 * kWsWaves)
 sparse_mla_fwd_ws_kernel(const FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[kStages * kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_score[2][kScoreBytes];   // tile parity
+  __shared__ __attribute__((aligned(16))) uint8_t s_p[2][kPBytes];    // tile parity
+  __shared__ __attribute__((aligned(16))) float s_mx[2][2][64];       // [parity][key block][head]
+  __shared__ __attribute__((aligned(16))) int s_flag[2][4];           // [parity][S wave]
+  __shared__ float s_alpha[64];                                       // O factors of a settle step
+  __shared__ float s_l[2][64];                                        // [key block][head] row sums
 
-  uint32_t* s_goff = (uint32_t*)s_score[0];   // index stage only
-  int* s_cnt = (int*)s_score[1];              // index stage only
+  uint32_t* s_goff = (uint32_t*)&s_p[0][0];   // index stage only (both P buffers)
+  int* s_cnt = (int*)&s_mx[0][0][0];          // index stage only
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool is_s = wave < 4;     // role (uniform per wave)
   const int sw = wave & 3;        // index within the role
-  const int hh = sw & 1;          // head half
-  const int kd = sw >> 1;         // S: key block; PV: value half
 
   const int64_t per_token = (int64_t)a.splits * a.head_blocks;
   const int64_t bid = blockIdx.x;
@@ -117,37 +150,14 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
   const int split = rem / a.head_blocks;
   const int hblock = rem % a.head_blocks;
 
-  // ---------------------------------------------------------------- 1. index stage
-  const int nvalid = build_key_list<PAGED, kWsWaves>(a, token, split, wave, lane, s_goff, s_cnt);
-  const int ntiles = (nvalid + kTileKeys - 1) / kTileKeys;
-
-  // S waves keep the offsets of rows 8sw .. 8sw+7 of every tile in registers:
-  // row r of tile t in lane 8(t & 7) + r of klist[t >> 3].
-  constexpr int kListRegs = kSegment / kTileKeys / 8;
-  uint32_t klist[kListRegs];
-#pragma unroll
-  for (int k = 0; k < kListRegs; ++k) {
-    const int n = 64 * k + lane, t = n >> 3, r = n & 7;
-    klist[k] = is_s && t < ntiles ? s_goff[t * kTileKeys + 8 * sw + r] : 0u;
-  }
-  __syncthreads();   // the score buffers are free from here on
-  const uint32_t stage_lds = lds_offset(s_stage);
-  const uint32_t score_lds = lds_offset(s_score[0]);
-  auto stage_of = [&](int t) { return stage_lds + (uint32_t)(t % kStages) * kStageBytes; };
-  // this head half's scores of tile t: [32 heads][32 keys]
-  auto scores_of = [&](int t) { return score_lds + (uint32_t)(t & 1) * kScoreBytes + (uint32_t)hh * (kScoreBytes / 2); };
-
-  // Barrier sequence, every wave:
-  //   prologue: tiles 0..2 gathered, tile 0 landed | scores of tile 0 written, tile 1 landed
-  //   tile j (j + 1 < ntiles): scores of tile j+1 written, tile j+2 landed
-  if (is_s) {
-    // ============================================================ S waves
-    const int hcol = lane & 15;   // 16x16 MFMA row / column
-    const int kq = lane >> 4;     // 16x16 MFMA k-group
-    // Q^T, head tile ht: dims 32c + 8kq .. +7 of head 16ht + hcol. Chunks 0..14
-    // in the accumulator file (the MFMA reads them from there), which with the
-    // QK^T accumulator (8) fills this wave's 128.
-    bf16x8_t qreg[2][kDqk / 32];
+  // S waves: head half hh, key block kd; lane = (hcol, kq) of the 16x16 MFMAs
+  const int hh = sw & 1, kd = sw >> 1;
+  const int hcol = lane & 15, kq = lane >> 4;
+  // Q^T (S waves), head tile ht: dims 32c + 8kq .. +7 of head 32hh + 16ht + hcol.
+  // Its loads are issued with the index loads so that the two latencies overlap.
+  bf16x8_t qreg[2][kDqk / 32];
+  auto load_q = [&] {
+    if (!is_s) return;
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
       const int h = hblock * 64 + hh * 32 + ht * 16 + hcol;
@@ -159,6 +169,35 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
         qreg[ht][c] = ok ? v : (bf16x8_t){};
       }
     }
+  };
+
+  // ---------------------------------------------------------------- 1. index stage
+  const int nvalid = build_key_list<PAGED, kWsWaves>(a, token, split, wave, lane, s_goff, s_cnt, load_q);
+  const int ntiles = (nvalid + kTileKeys - 1) / kTileKeys;
+
+  // PV waves keep the offsets of rows 8sw .. 8sw+7 of every tile in registers:
+  // row r of tile t in lane 8(t & 7) + r of klist[t >> 3].
+  constexpr int kListRegs = kSegment / kTileKeys / 8;
+  uint32_t klist[kListRegs];
+#pragma unroll
+  for (int k = 0; k < kListRegs; ++k) {
+    const int n = 64 * k + lane, t = n >> 3, r = n & 7;
+    klist[k] = !is_s && t < ntiles ? s_goff[t * kTileKeys + 8 * sw + r] : 0u;
+  }
+  __syncthreads();   // the P buffers and block maxima are free from here on
+  const uint32_t stage_lds = lds_offset(s_stage);
+  const uint32_t p_lds = lds_offset(&s_p[0][0]);
+  auto stage_of = [&](int t) { return stage_lds + (uint32_t)(t % kStages) * kStageBytes; };
+  auto p_of = [&](int t) { return p_lds + (uint32_t)(t & 1) * kPBytes; };
+
+  // Barrier sequence, every wave:
+  //   prologue: tiles 0..2 gathered, tile 0 landed | tile 0 scored, tile 1 landed
+  //   tile j: [settle step, if a flag of tile j is set] | tile j+1 scored, tile j+2 landed (j + 1 < ntiles)
+  //   epilogue: row sums published
+  if (is_s) {
+    // ============================================================ S waves
+    // Q^T chunks 0..14 in the accumulator file (the MFMA reads them from
+    // there), which with the QK^T accumulator (8) fills this wave's 128.
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
@@ -166,14 +205,169 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
         if (c < 15) asm volatile("" : "+a"(qreg[ht][c]));
         else asm volatile("" : "+v"(qreg[ht][c]));
       }
-    // K operand, latent chunk c: row 16kd + hcol, logical granule 4c + kq:
+    // K operand, latent chunk c: row 16kd + key_rho(hcol), logical granule 4c + kq:
     //   (kb0 ^ 64(c & 3)) + 256(c >> 2);  rope chunk 16 + cr: rb0 ^ 64cr
-    const int kr_row = 16 * kd + hcol;
+    const int kr_row = 16 * kd + key_rho(hcol);
+    const int kq_key = 4 * key_sigma(kq);   // this lane's scores: keys 16kd + kq_key .. +3
     const uint32_t kb0 = kr_row * 1024 + 16 * (kq ^ swz_ws(kr_row));
     const uint32_t rb0 = kRopeOff + kr_row * 128 + 16 * (kq ^ ((kr_row >> 1) & 7));
     auto kread = [&](uint32_t st, int c) {
       return c < 16 ? lds_b128_at(((st + kb0) ^ (64u * (c & 3))) + 256u * (c >> 2))
                     : lds_b128_at((st + rb0) ^ (64u * (c - 16)));
+    };
+
+    // per head tile ht (head 32hh + 16ht + hcol): reference, row sum of the
+    // settled tiles, and the last scored tile's scaled scores (keys
+    // 16kd + kq_key .. +3, masked = -inf) with their numerator sum
+    float m_ref[2] = {-INFINITY, -INFINITY};
+    float l_run[2] = {0.f, 0.f};
+    float sv[2][4];
+    float psum[2] = {0.f, 0.f};
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[ht][i] = -INFINITY;
+
+    // numerators of the scored tile t under the current references -> P buffer
+    auto make_p = [&](int t) {
+      const uint32_t pb = p_of(t);
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[ht][i] - m_ref[ht]);
+        psum[ht] = (p[0] + p[1]) + (p[2] + p[3]);
+        const u32x2_t w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+        lds_write_b64_at(pb + p_off(32 * hh + 16 * ht + hcol, (16 * kd + kq_key) >> 3) + 2 * (kq_key & 7), w);
+      }
+    };
+    // settle tile t (its P written, flags published at the last barrier)
+    auto settle = [&](int t, int4 fl) {
+      if ((fl.x | fl.y | fl.z | fl.w) != 0) {   // same in every wave of the workgroup
+        const int b = t & 1;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          const int h = 32 * hh + 16 * ht + hcol;
+          const float mn = next_ref(m_ref[ht], fmaxf(s_mx[b][0][h], s_mx[b][1][h]));
+          const float al = ref_factor(m_ref[ht], mn);
+          m_ref[ht] = mn;
+          l_run[ht] *= al;
+          if (kd == 0 && kq == 0) s_alpha[h] = al;
+        }
+        make_p(t);
+        __syncthreads();   // new P and O factors visible
+      }
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) l_run[ht] += psum[ht];
+    };
+    // QK^T of tile ts, then its scaled scores, block maxima, flag and P;
+    // tile tsettle (if any) is settled once the first K operands are in flight
+    auto s_step = [&](int ts, int tsettle) {
+      constexpr int kS = 36;    // chunk t >> 1, head tile t & 1
+      constexpr int kKA = 10;   // K chunks read ahead (about 320 MFMA clocks)
+      const uint32_t st = stage_of(ts);
+      int4 fl = {0, 0, 0, 0};
+      if (tsettle >= 0) fl = *(const int4*)&s_flag[tsettle & 1][0];
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8_t kr[kKA + 1];
+#pragma unroll
+      for (int c = 0; c < kKA; ++c) kr[c] = kread(st, c);
+      __builtin_amdgcn_sched_barrier(0);
+      if (tsettle >= 0) settle(tsettle, fl);
+      float4_t sacc[2];
+#pragma unroll
+      for (int t = 0; t < kS; ++t) {
+        const int c = t >> 1;
+        if ((t & 1) == 0 && c + kKA < kS / 2) kr[(c + kKA) % (kKA + 1)] = kread(st, c + kKA);
+        sacc[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[c % (kKA + 1)], qreg[t & 1][c],
+                                                              c == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : sacc[t & 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const bool partial = (ts + 1) * kTileKeys > nvalid;   // uniform
+      const int key0 = ts * kTileKeys + 16 * kd + kq_key;
+      bool exceed = false;
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = sacc[ht][i] * a.scale_log2;
+          sv[ht][i] = partial && key0 + i >= nvalid ? -INFINITY : x;
+        }
+        const float ml = fmaxf(fmaxf(sv[ht][0], sv[ht][1]), fmaxf(sv[ht][2], sv[ht][3]));
+        exceed = exceed || ml > m_ref[ht] + kWsSlack;
+        const float mx = max_kgroups(ml);
+        if (kq == 0) s_mx[ts & 1][kd][32 * hh + 16 * ht + hcol] = mx;
+      }
+      const bool any = __ballot(exceed) != 0;
+      if (lane == 0) s_flag[ts & 1][sw] = any ? 1 : 0;
+      make_p(ts);
+    };
+
+    if (ntiles > 0) {
+      __syncthreads();   // tile 0 landed
+      s_step(0, -1);
+      __syncthreads();   // tile 0 scored, tile 1 landed
+      for (int j = 0; j + 1 < ntiles; ++j) {
+        s_step(j + 1, j);
+        __syncthreads();
+      }
+      settle(ntiles - 1, *(const int4*)&s_flag[(ntiles - 1) & 1][0]);
+    }
+
+    // ---------------------------------------------------------------- 6. epilogue (LSE)
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const float lw = sum_kgroups(l_run[ht]);   // this key block's keys of the head
+      if (kq == 0) s_l[kd][32 * hh + 16 * ht + hcol] = lw;
+    }
+    __syncthreads();   // row sums published
+    if (kd == 0 && kq == 0) {
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        const int h = 32 * hh + 16 * ht + hcol;
+        const int head = hblock * 64 + h;
+        if (head < a.num_heads) {
+          const float L = s_l[0][h] + s_l[1][h];
+          if (a.splits == 1) {
+            a.lse[token * a.lse_st + head] = L > 0.f ? (m_ref[ht] + __log2f(L)) * kLn2 : -INFINITY;
+          } else {
+            const int64_t prow = (token * a.splits + split) * a.num_heads + head;
+            a.part_ml[prow * 2] = m_ref[ht];
+            a.part_ml[prow * 2 + 1] = L;
+          }
+        }
+      }
+    }
+  } else {
+    // ============================================================ PV waves
+    const int pw = sw;           // value columns 128pw .. 128pw+127
+    const int col = lane & 31;   // 32x32 MFMA column: head 32ht2 + col
+    const int kh = lane >> 5;    // 32x32 MFMA k half
+    float16_t oacc[2][4];        // O^T: [head tile ht2][value tile u]
+#pragma unroll
+    for (int ht2 = 0; ht2 < 2; ++ht2)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        oacc[ht2][u] = (float16_t){};
+        asm volatile("" : "+a"(oacc[ht2][u]));
+      }
+    // V^T operand of value tile u and key block m, read rd: the lane (group
+    // vg = (lane >> 4) & 1, index vj = lane & 15) points at row 16m + 8kh + 4rd + vj/4,
+    // columns 128pw + 32u + 16vg + 4(vj & 3) .. +3; the transposed read returns
+    // column 128pw + 32u + 16vg + vj (operand row col) of keys 16m + 8kh + 4rd .. +3
+    // (operand slots 4rd .. 4rd+3). Address: (vb0[rd] ^ 64u) + 16384m
+    const int vj = lane & 15, vg = (lane >> 4) & 1;
+    uint32_t vb0[2];
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int r = 8 * kh + 4 * rd + (vj >> 2);
+      vb0[rd] = r * 1024 + 256 * pw + 16 * ((2 * vg + ((vj & 3) >> 1)) ^ swz_ws(r)) + 8 * (vj & 1);
+    }
+    auto vread = [&](uint32_t st, int u, int m) {
+      const uint32_t off = 16384u * m;
+      const short4_t lo = lds_tr16_at(((st + vb0[0]) ^ (64u * u)) + off);
+      const short4_t hi = lds_tr16_at(((st + vb0[1]) ^ (64u * u)) + off);
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     const uint32_t lane16 = (uint32_t)lane * 16u;
     uint32_t grope = 0;
@@ -186,18 +380,18 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
       for (int r = 0; r < 8; ++r) go[r] = __builtin_amdgcn_readlane(klist[0], 8 * (t & 7) + r);
       grope = (uint32_t)__builtin_amdgcn_ds_bpermute((8 * (t & 7) + (lane >> 3)) * 4, (int)klist[0]);
     };
-    // copy d of this wave's share of tile t: latent row 8sw + d (d < 8), or
-    // rope rows 8sw .. 8sw+7 (lane i: rope granule (i & 7) ^ ((row >> 1) & 7) of row 8sw + i/8)
+    // copy d of this wave's share of tile t: latent row 8pw + d (d < 8), or
+    // rope rows 8pw .. 8pw+7 (lane i: rope granule (i & 7) ^ ((row >> 1) & 7) of row 8pw + i/8)
     auto gather_copy = [&](int t, const uint32_t* go, int d) {
       const uint32_t base = stage_of(t);
       if (d < 8) {
-        const int row = 8 * sw + d;
+        const int row = 8 * pw + d;
         dma_16b_sbase((uint64_t)a.kv + (uint64_t)go[d] * 16ull, lane16 ^ (uint32_t)(swz_ws(row) * 16),
                       base + row * 1024);
       } else {
-        const int rrow = 8 * sw + (lane >> 3);
+        const int rrow = 8 * pw + (lane >> 3);
         const int g = (lane & 7) ^ ((rrow >> 1) & 7);
-        dma_16b(a.kv + ((uint64_t)grope + 64u + (uint32_t)g) * 16ull, base + kRopeOff + sw * 1024);
+        dma_16b(a.kv + ((uint64_t)grope + 64u + (uint32_t)g) * 16ull, base + kRopeOff + pw * 1024);
       }
     };
     auto issue = [&](int t) {   // all of this wave's copies of tile t (prologue)
@@ -206,31 +400,59 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
 #pragma unroll
       for (int d = 0; d < kDmaPerWave; ++d) gather_copy(t, go, d);
     };
-    // QK^T of tile ts (the gather of tile ti spread over it); the raw scores
-    // of head 16ht + hcol, keys 16kd + 4kq .. +3 (group 4kd + kq) go to the
-    // score buffer of tile ts.
-    auto s_step = [&](int ts, int ti) {
-      constexpr int kS = 36;    // chunk t >> 1, head tile t & 1
-      constexpr int kKA = 8;    // K chunks read ahead (about 256 MFMA clocks)
-      const uint32_t st = stage_of(ts);
+    // P^T operand of head tile ht2 and key block m: head 32ht2 + col, keys 16m + 8kh .. +7
+    auto read_p = [&](uint32_t pb, bf16x8_t (*pk)[2]) {
+#pragma unroll
+      for (int ht2 = 0; ht2 < 2; ++ht2)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) pk[ht2][m] = lds_b128_at(pb + p_off(32 * ht2 + col, 2 * m + kh));
+    };
+    // PV of tile t, with the gather of tile tg (if any) spread over it
+    auto pv_tile = [&](int t, int tg) {
+      constexpr int kO = 8;    // V^T operands: key block o >> 2, value tile o & 3
+      constexpr int kVA = 4;   // operands read ahead (8 LDS operations)
+      const uint32_t st = stage_of(t);
+      const uint32_t pb = p_of(t);
+      const int4 fl = *(const int4*)&s_flag[t & 1][0];
+      bf16x8_t pk[2][2];
+      read_p(pb, pk);
+      bf16x8_t vr[kVA + 1];
+#pragma unroll
+      for (int o = 0; o < kVA; ++o) vr[o] = vread(st, o & 3, o >> 2);
       uint32_t go[8];
-      gather_rows(ti >= 0 ? ti : 0, go, ti >= 0);
-      bf16x8_t kr[kKA + 1];
-      float4_t sacc[2];
+      gather_rows(tg >= 0 ? tg : 0, go, tg >= 0);
+      if ((fl.x | fl.y | fl.z | fl.w) != 0) {   // settle step: new P, O factors
+        __syncthreads();
+        float al[2];
 #pragma unroll
-      for (int c = 0; c < kKA; ++c) kr[c] = kread(st, c);
+        for (int ht2 = 0; ht2 < 2; ++ht2) al[ht2] = s_alpha[32 * ht2 + col];
+        read_p(pb, pk);
+        if (__ballot(al[0] != 1.f || al[1] != 1.f)) {
 #pragma unroll
-      for (int t = 0; t < kS; ++t) {
-        const int c = t >> 1;
-        if ((t & 1) == 0 && c + kKA < kS / 2) kr[(c + kKA) % (kKA + 1)] = kread(st, c + kKA);
-        sacc[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[c % (kKA + 1)], qreg[t & 1][c],
-                                                              c == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : sacc[t & 1], 0, 0, 0);
-        if (ti >= 0 && t % 4 == 1 && t / 4 < kDmaPerWave) gather_copy(ti, go, t / 4);   // copies at MFMA 1, 5, .., 33
+          for (int ht2 = 0; ht2 < 2; ++ht2)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              float16_t x = oacc[ht2][u];
+              asm volatile("" : "+v"(x));
+              x *= al[ht2];
+              asm volatile("" : "+a"(x));
+              oacc[ht2][u] = x;
+            }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 2 * kO; ++s) {
+        const int o = s >> 1, ht2 = s & 1;
+        if (ht2 == 0 && o + kVA < kO) vr[(o + kVA) % (kVA + 1)] = vread(st, (o + kVA) & 3, (o + kVA) >> 2);
+        oacc[ht2][o & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[o % (kVA + 1)], pk[ht2][o >> 2], oacc[ht2][o & 3], 0, 0, 0);
+        if (tg >= 0 && s < kDmaPerWave) gather_copy(tg, go, s);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const uint32_t sb = scores_of(ts);
 #pragma unroll
-      for (int ht = 0; ht < 2; ++ht) lds_f4_write_at(sb + score_off(16 * ht + hcol, 4 * kd + kq), sacc[ht]);
+      for (int ht2 = 0; ht2 < 2; ++ht2)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) asm volatile("" : "+a"(oacc[ht2][u]));
     };
 
     if (ntiles > 0) {
@@ -240,170 +462,69 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
       if (ntiles > 2) wait_vmem<2 * kDmaPerWave>();
       else if (ntiles > 1) wait_vmem<kDmaPerWave>();
       else wait_vmem<0>();
-      __syncthreads();
-      s_step(0, -1);
-      if (ntiles > 2) wait_vmem<kDmaPerWave>();   // tile 1 landed
+      __syncthreads();   // tile 0 landed
+      if (ntiles > 2) wait_vmem<kDmaPerWave>();
       else wait_vmem<0>();
-      __syncthreads();
+      __syncthreads();   // tile 0 scored, tile 1 landed
       for (int j = 0; j + 1 < ntiles; ++j) {
-        // QK^T of tile j+1; the gather of tile j+3 goes into the stage of tile
-        // j-1 and the scores into the buffer of tile j-1, both of which the PV
-        // waves left at the last barrier
-        s_step(j + 1, j + 3 < ntiles ? j + 3 : -1);
+        // the gather of tile j+3 goes into the stage of tile j-1, which every
+        // wave left at the last barrier
+        pv_tile(j, j + 3 < ntiles ? j + 3 : -1);
         if (j + 3 < ntiles) wait_vmem<kDmaPerWave>();   // tile j+2 landed; tile j+3 may still fly
         else wait_vmem<0>();
         __syncthreads();
       }
-    }
-  } else {
-    // ============================================================ PV waves
-    const int col = lane & 31;   // 32x32 MFMA column: head col of the head half
-    const int kh = lane >> 5;    // 32x32 MFMA k half
-    float m_run = -INFINITY;     // reference of head col, log2 units
-    float l_run = 0.f;           // sum over this lane's keys (16 of every tile)
-    float16_t oacc[8];           // O^T: value tile u of this half; lane holds head col
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      oacc[u] = (float16_t){};
-      asm volatile("" : "+a"(oacc[u]));
-    }
-    // V^T operand of value tile u and key block m, read rd: the lane (group
-    // vg = (lane >> 4) & 1, index vj = lane & 15) points at row 16m + 8kh + 4rd + vj/4,
-    // columns 256kd + 32u + 16vg + 4(vj & 3) .. +3; the transposed read returns
-    // column 256kd + 32u + 16vg + vj (operand row col) of keys 16m + 8kh + 4rd .. +3
-    // (operand slots 4rd .. 4rd+3). Address: ((vb0[rd] ^ 64(u & 3)) + 16384m + 256(u >> 2))
-    const int vj = lane & 15, vg = (lane >> 4) & 1;
-    uint32_t vb0[2];
-#pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-      const int r = 8 * kh + 4 * rd + (vj >> 2);
-      vb0[rd] = r * 1024 + 512 * kd + 16 * ((2 * vg + ((vj & 3) >> 1)) ^ swz_ws(r)) + 8 * (vj & 1);
-    }
-    auto vread = [&](uint32_t st, int u, int m) {
-      const uint32_t off = 16384u * m + 256u * (u >> 2);
-      const short4_t lo = lds_tr16_at(((st + vb0[0]) ^ (64u * (u & 3))) + off);
-      const short4_t hi = lds_tr16_at(((st + vb0[1]) ^ (64u * (u & 3))) + off);
-      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    // Tile t: online softmax of this lane's 16 scores (head col; slot 8m + e
-    // holds key 16m + 8kh + e) into the P^T operands, then PV.
-    auto pv_tile = [&](int t) {
-      constexpr int kP = 16;   // PV MFMAs: key block s >> 3, value tile s & 7
-      constexpr int kVA = 6;   // V^T operands read ahead (12 LDS operations)
-      const uint32_t st = stage_of(t);
-      const uint32_t sb = scores_of(t);
-      float4_t sc[4];   // group 4(q >> 1) + 2kh + (q & 1): keys 16(q >> 1) + 8kh + 4(q & 1) .. +3
-#pragma unroll
-      for (int q = 0; q < 4; ++q) sc[q] = lds_f4_at(sb + score_off(col, 4 * (q >> 1) + 2 * kh + (q & 1)));
-      bf16x8_t vr[kVA + 1];
-#pragma unroll
-      for (int s = 0; s < kVA; ++s) vr[s] = vread(st, s & 7, s >> 3);
-      float sv[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[4 * q + i] = sc[q][i];
-      const bool partial = (t + 1) * kTileKeys > nvalid;   // uniform
-      auto key_ok = [&](int k) { return t * kTileKeys + 16 * (k >> 3) + 8 * kh + (k & 7) < nvalid; };
-      if (partial) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-          if (!key_ok(k)) sv[k] = -INFINITY;
-      }
-      float mx = sv[0];
-#pragma unroll
-      for (int k = 1; k < 16; ++k) mx = fmaxf(mx, sv[k]);
-      mx = max_halves(mx);   // all 32 keys of the tile, which holds at least one valid key
-      mx = mx == -INFINITY ? -INFINITY : mx * a.scale_log2;   // the scale may be 0
-      const float m_new = next_ref(m_run, mx);
-      const float alpha = ref_factor(m_run, m_new);
-      m_run = m_new;
-      float p[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) p[k] = fast_exp2(__builtin_fmaf(sv[k], a.scale_log2, -m_run));
-      if (partial) {   // a masked slot has weight 0, also when the scale is 0
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-          if (!key_ok(k)) p[k] = 0.f;
-      }
-      float ps = 0.f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) ps += p[k];
-      l_run = l_run * alpha + ps;
-      bf16x8_t pk[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        uint4 w;
-        w.x = pack_bf16x2(p[8 * m + 0], p[8 * m + 1]);
-        w.y = pack_bf16x2(p[8 * m + 2], p[8 * m + 3]);
-        w.z = pack_bf16x2(p[8 * m + 4], p[8 * m + 5]);
-        w.w = pack_bf16x2(p[8 * m + 6], p[8 * m + 7]);
-        pk[m] = __builtin_bit_cast(bf16x8_t, w);
-      }
-      if (__ballot(alpha != 1.f)) {   // some reference moved: rescale O
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          float16_t x = oacc[u];
-          asm volatile("" : "+v"(x));
-          x *= alpha;
-          asm volatile("" : "+a"(x));
-          oacc[u] = x;
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s = 0; s < kP; ++s) {
-        if (s + kVA < kP) vr[(s + kVA) % (kVA + 1)] = vread(st, (s + kVA) & 7, (s + kVA) >> 3);
-        oacc[s & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[s % (kVA + 1)], pk[s >> 3], oacc[s & 7], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) asm volatile("" : "+a"(oacc[u]));
-    };
-
-    if (ntiles > 0) {
-      __syncthreads();   // tile 0 landed
-      __syncthreads();   // scores of tile 0 written, tile 1 landed
-      for (int j = 0; j + 1 < ntiles; ++j) {
-        pv_tile(j);
-        __syncthreads();
-      }
-      pv_tile(ntiles - 1);
+      pv_tile(ntiles - 1, -1);
     }
 
-    // ---------------------------------------------------------------- 6. epilogue
-    const float L = sum_halves(l_run);   // all keys of head col
-    const float inv_l = L > 0.f ? 1.f / L : 0.f;
-    const int head = hblock * 64 + hh * 32 + col;
-    if (head < a.num_heads) {
-      if (a.splits == 1) {
-        uint16_t* op = a.out + token * a.o_st + (int64_t)head * a.o_sh + 256 * kd + 4 * kh;
+    // ---------------------------------------------------------------- 6. epilogue (O)
+    // Normalised O goes to LDS (the tile ring is idle now) as [head][column]
+    // rows, so that the global stores below write whole rows. bf16: 1 KB per
+    // head, 16-byte granule G at G ^ (head & 15); fp32 partials: 2 KB per head.
+    __syncthreads();   // row sums published; every stage read and copy done
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float16_t x = oacc[u] * inv_l;
+    for (int ht2 = 0; ht2 < 2; ++ht2) {
+      const int h = 32 * ht2 + col;
+      const float L = s_l[0][h] + s_l[1][h];
+      const float inv_l = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            uint2 w;
-            w.x = pack_bf16x2(x[4 * q4], x[4 * q4 + 1]);
-            w.y = pack_bf16x2(x[4 * q4 + 2], x[4 * q4 + 3]);
-            *(uint2*)(op + 32 * u + 8 * q4) = w;   // O[head][256kd + 32u + 8q4 + 4kh .. +3]
+      for (int u = 0; u < 4; ++u) {
+        const float16_t x = oacc[ht2][u] * inv_l;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int c0 = 128 * pw + 32 * u + 8 * q4 + 4 * kh;   // columns c0 .. c0+3
+          if (a.splits == 1) {
+            const u32x2_t w = {pack_bf16x2(x[4 * q4], x[4 * q4 + 1]), pack_bf16x2(x[4 * q4 + 2], x[4 * q4 + 3])};
+            lds_write_b64_at(stage_lds + h * 1024 + 16 * ((c0 >> 3) ^ (h & 15)) + 2 * (c0 & 7), w);
+          } else {
+            *(__attribute__((address_space(3))) float4_t*)(uintptr_t)(stage_lds + h * 2048 + 16 * ((c0 >> 2) ^ (h & 15))) =
+                (float4_t){x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
           }
         }
-        if (kd == 0 && kh == 0) a.lse[token * a.lse_st + head] = L > 0.f ? (m_run + __log2f(L)) * kLn2 : -INFINITY;
-      } else {
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- 7. O stores (all waves)
+  __syncthreads();   // O staged
+  const int tid = threadIdx.x;
+  if (a.splits == 1) {
+#pragma unroll
+    for (int k = 0; k < 64 * 64 / (64 * kWsWaves); ++k) {
+      const int flat = k * 64 * kWsWaves + tid, h = flat >> 6, g = flat & 63;   // one head row per wave
+      const int head = hblock * 64 + h;
+      const bf16x8_t v = lds_b128_at(lds_offset(s_stage) + h * 1024 + 16 * (g ^ (h & 15)));
+      if (head < a.num_heads) *(bf16x8_t*)(a.out + token * a.o_st + (int64_t)head * a.o_sh + 8 * g) = v;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 64 * 128 / (64 * kWsWaves); ++k) {
+      const int flat = k * 64 * kWsWaves + tid, h = flat >> 7, g = flat & 127;
+      const int head = hblock * 64 + h;
+      const float4_t v = *(__attribute__((address_space(3))) const float4_t*)(uintptr_t)(lds_offset(s_stage) + h * 2048 + 16 * (g ^ (h & 15)));
+      if (head < a.num_heads) {
         const int64_t prow = (token * a.splits + split) * a.num_heads + head;
-        float* pp = a.part_o + prow * kDv + 256 * kd + 4 * kh;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float16_t x = oacc[u] * inv_l;
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *(float4_t*)(pp + 32 * u + 8 * q4) = (float4_t){x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
-        }
-        if (kd == 0 && kh == 0) {
-          a.part_ml[prow * 2] = m_run;
-          a.part_ml[prow * 2 + 1] = L;
-        }
+        *(float4_t*)(a.part_o + prow * kDv + 4 * g) = v;
       }
     }
   }
