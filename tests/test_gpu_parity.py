@@ -186,25 +186,60 @@ def test_duplicate_indices_count_twice():
     check(np32(out), np32(lse), *ref_flat(q, kv, idx, 0.05), "duplicates")
 
 
-def test_peaky_scores_stay_finite():
-    q, kv, idx = random_case(T=32, H=8, N=2000, topk=512, seed=12, junk=False)
+@pytest.mark.parametrize("H", [8, 64])
+def test_peaky_scores_stay_finite(H):
+    q, kv, idx = random_case(T=32, H=H, N=2000, topk=512, seed=12, junk=False)
     q = (q.float() * 30).to(torch.bfloat16)
     out, lse = run_flat(q, kv, idx, 1 / 24)
     assert torch.isfinite(out.float()).all()
-    check(np32(out), np32(lse), *ref_flat(q, kv, idx, 1 / 24), "peaky")
+    check(np32(out), np32(lse), *ref_flat(q, kv, idx, 1 / 24), f"peaky H={H}")
 
 
+@pytest.mark.parametrize("H", [16, 64])
 @pytest.mark.parametrize("sm", [0.0, 1e-4, 0.5])
-def test_softmax_scale_range(sm):
+def test_softmax_scale_range(sm, H):
     """sm_scale = 0 gives uniform weights (O = mean of the latent rows, LSE =
     log of the key count); a large scale makes every row nearly one-hot."""
-    q, kv, idx = random_case(T=40, H=16, N=3000, topk=700, seed=13)
+    q, kv, idx = random_case(T=40, H=H, N=3000, topk=700, seed=13)
     out, lse = run_flat(q, kv, idx, sm)
     ro, rl = ref_flat(q, kv, idx, sm)
-    check(np32(out), np32(lse), ro, rl, f"scale{sm}")
+    check(np32(out), np32(lse), ro, rl, f"scale{sm} H={H}")
     if sm == 0.0:
         n = ((idx >= 0) & (idx < 3000)).sum(1).numpy()
-        np.testing.assert_allclose(np32(lse), np.log(n)[:, None].repeat(16, 1), rtol=1e-6, atol=1e-6)
+        np.testing.assert_allclose(np32(lse), np.log(n)[:, None].repeat(H, 1), rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("H", [8, 64])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_rising_scores_move_the_reference(H, splits):
+    """Scores that climb along the key list (key j at about 200 * j / topk,
+    natural-log units) force the running maximum to move many times inside a
+    row, by more than any lazy-rescale slack, so every rescale path of O and
+    of the row sum runs; per row the first keys then weigh ~e^-200."""
+    T, N, topk = 12, 2048, 1500
+    g = torch.Generator().manual_seed(21)
+    u = torch.randn(576, generator=g)
+    q = (u[None, None, :] + 0.3 * torch.randn((T, H, 576), generator=g)).to(torch.bfloat16)
+    ramp = torch.arange(N, dtype=torch.float32) / topk
+    kv = (8.3 * ramp[:, None] * u[None, :] + 0.5 * torch.randn((N, 576), generator=g)).to(torch.bfloat16)
+    idx = torch.arange(topk, dtype=torch.int32).repeat(T, 1)
+    idx[1::2] = torch.flip(idx[1::2], dims=[1])   # falling order too: the maximum comes first
+    out, lse = run_flat(q, kv, idx, 1 / 24, num_splits=splits)
+    check(np32(out), np32(lse), *ref_flat(q, kv, idx, 1 / 24), f"rising H={H} splits={splits}")
+
+
+def test_paged_wide_heads():
+    """The 64-head kernel on the paged cache (page mapping fused in the index stage)."""
+    d = workloads.make_paged(num_seqs=3, q_per_seq=4, num_heads=64, min_len=1500, max_len=4000, topk=1024)
+    dev = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in d.items()}
+    out, lse = _dsa().sparse_mla_fwd_paged(dev["q"], dev["kv_pages"], dev["page_table"],
+                                           dev["seq_lens"], dev["indices"], d["sm_scale"],
+                                           d["q_per_seq"])
+    torch.cuda.synchronize()
+    ro, rl = sparse_mla_fwd_paged_ref(np32(d["q"]), np32(d["kv_pages"]), d["page_table"].numpy(),
+                                      d["seq_lens"].numpy(), d["indices"].numpy(), d["sm_scale"],
+                                      d["q_per_seq"])
+    check(np32(out), np32(lse), ro, rl, "paged H=64")
 
 
 def test_strided_inputs_and_outputs():
