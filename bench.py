@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -58,6 +59,7 @@ def traffic_for(workload: str):
 
 
 COPY_BYTES = 256 << 20   # the calibration copy reads and writes this many bytes
+FWD_KERNEL = re.compile(r"sparse_mla_fwd(_ws)?_kernel")   # the forward kernels' names
 
 
 def copy_calibration(dev, reps: int = 3):
@@ -94,7 +96,7 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: st
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         vals = per_dispatch(path, counter)
         copy = [v for (d, k), v in vals.items() if "neg" in k]
-        fwd = [v for (d, k), v in vals.items() if "sparse_mla_fwd_kernel" in k]
+        fwd = [v for (d, k), v in vals.items() if FWD_KERNEL.search(k)]
         if not copy or not fwd:
             raise SystemExit(f"{path}: no calibration copy or forward dispatch with {counter}")
         factor = COPY_BYTES / (statistics.median(copy) * 1024.0)
