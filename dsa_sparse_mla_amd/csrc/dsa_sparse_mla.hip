@@ -58,15 +58,15 @@ int head_blocks(int32_t H) { return (H + 16 * head_tiles(H) - 1) / (16 * head_ti
 
 // Splits of each index row: at least ceil(topk / 2048); for a large enough
 // problem, doubled while the grid holds fewer than two workgroups per CU
-// (one workgroup fills a CU, and a second hides its start-up and tail) and
-// each split keeps at least 128 entries.
+// (one workgroup fills a CU, and a second hides its start-up and tail),
+// while each split keeps at least 128 entries and the count stays <= 64.
 int choose_splits(int64_t T, int32_t H, int32_t topk, int32_t requested, int cus) {
   const int smin = (topk + dsa::kSegment - 1) / dsa::kSegment;
   if (requested > 0) return requested;
   int s = smin;
   if (T * (int64_t)topk >= (int64_t)256 * 1024) {
     const int64_t per_split = T * head_blocks(H);
-    while (per_split * s < 2LL * cus && (int64_t)s * 2 * 128 <= topk && s < 64) s *= 2;
+    while (per_split * s < 2LL * cus && (int64_t)s * 2 * 128 <= topk && s * 2 <= 64) s *= 2;
   }
   return s;
 }

@@ -152,6 +152,29 @@ def test_workspace_query(T, H, topk, req, splits, nbytes):
         assert s >= 3 and b == T * s * H * 514 * 4   # at least ceil(5000 / 2048) splits
 
 
+@pytest.mark.parametrize("T,H,topk,splits", [
+    (384, 8, 2048, 2),      # paged decode: 384 rows fill 2 x 256 CUs only with two splits
+    (2119, 8, 2048, 1),     # prefill with enough tokens: never split
+    (8192, 64, 2048, 1),
+    (130, 8, 2048, 4),      # doubles while tokens x splits < 2 x CUs (130, 260 -> 520)
+    (128, 8, 2048, 4),      # 128 x 2048 entries: exactly the size that starts splitting
+    (127, 8, 2048, 1),      # one row fewer: too small to pay the merge
+    (200, 128, 2048, 2),    # two head blocks count as two workgroups per token
+    (100, 8, 4096, 8),      # rows over 2048 entries start at 2 splits, then double
+    (3, 8, 60000, 30),      # long rows: ceil(topk / 2048) splits; too few entries to double
+    (5, 8, 60000, 60),      # 30 doubles once; 120 would pass the 64-split cap
+    (10, 8, 60000, 60),
+])
+def test_split_policy(T, H, topk, splits):
+    """Automatic split count (no GPU here: the host logic assumes 256 CUs,
+    the MI355X count): splits double from ceil(topk / 2048) while
+    T x head_blocks x splits < 2 x CUs, for calls of at least 256K index
+    entries, keeping >= 128 keys per split and at most 64 splits."""
+    s, b = binding.workspace_size(T, H, topk, 0)
+    assert s == splits
+    assert b == (T * s * H * 514 * 4 if s > 1 else 0)
+
+
 def test_workspace_query_rejects_bad_sizes():
     with pytest.raises(binding.DsaError):
         binding.workspace_size(10, 0, 2048, 0)
