@@ -44,6 +44,8 @@
 // (xtuner PR 2083), Runtime constraints.
 #pragma once
 
+#include <type_traits>
+
 #include "fwd_kernel.hpp"
 
 namespace dsa {
@@ -382,8 +384,7 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
     };
     // copy d of this wave's share of tile t: latent row 8pw + d (d < 8), or
     // rope rows 8pw .. 8pw+7 (lane i: rope granule (i & 7) ^ ((row >> 1) & 7) of row 8pw + i/8)
-    auto gather_copy = [&](int t, const uint32_t* go, int d) {
-      const uint32_t base = stage_of(t);
+    auto gather_copy = [&](uint32_t base, const uint32_t* go, int d) {   // base: the stage, in SGPRs
       if (d < 8) {
         const int row = 8 * pw + d;
         dma_16b_sbase((uint64_t)a.kv + (uint64_t)go[d] * 16ull, lane16 ^ (uint32_t)(swz_ws(row) * 16),
@@ -397,8 +398,9 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
     auto issue = [&](int t) {   // all of this wave's copies of tile t (prologue)
       uint32_t go[8];
       gather_rows(t, go, true);
+      const uint32_t base = __builtin_amdgcn_readfirstlane(stage_of(t));
 #pragma unroll
-      for (int d = 0; d < kDmaPerWave; ++d) gather_copy(t, go, d);
+      for (int d = 0; d < kDmaPerWave; ++d) gather_copy(base, go, d);
     };
     // P^T operand of head tile ht2 and key block m: head 32ht2 + col, keys 16m + 8kh .. +7
     auto read_p = [&](uint32_t pb, bf16x8_t (*pk)[2]) {
@@ -407,8 +409,10 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) pk[ht2][m] = lds_b128_at(pb + p_off(32 * ht2 + col, 2 * m + kh));
     };
-    // PV of tile t, with the gather of tile tg (if any) spread over it
-    auto pv_tile = [&](int t, int tg) {
+    // PV of tile t, with the gather of tile tg spread over it if G (one copy
+    // of the body per case, so the MFMA stream carries no branches)
+    auto pv_tile = [&](auto gather, int t, int tg) {
+      constexpr bool G = decltype(gather)::value;
       constexpr int kO = 8;    // V^T operands: key block o >> 2, value tile o & 3
       constexpr int kVA = 4;   // operands read ahead (8 LDS operations)
       const uint32_t st = stage_of(t);
@@ -420,7 +424,11 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
 #pragma unroll
       for (int o = 0; o < kVA; ++o) vr[o] = vread(st, o & 3, o >> 2);
       uint32_t go[8];
-      gather_rows(tg >= 0 ? tg : 0, go, tg >= 0);
+      uint32_t gbase = 0;
+      if (G) {
+        gather_rows(tg, go, true);
+        gbase = __builtin_amdgcn_readfirstlane(stage_of(tg));
+      }
       if ((fl.x | fl.y | fl.z | fl.w) != 0) {   // settle step: new P, O factors
         __syncthreads();
         float al[2];
@@ -446,7 +454,7 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
         const int o = s >> 1, ht2 = s & 1;
         if (ht2 == 0 && o + kVA < kO) vr[(o + kVA) % (kVA + 1)] = vread(st, (o + kVA) & 3, (o + kVA) >> 2);
         oacc[ht2][o & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[o % (kVA + 1)], pk[ht2][o >> 2], oacc[ht2][o & 3], 0, 0, 0);
-        if (tg >= 0 && s < kDmaPerWave) gather_copy(tg, go, s);
+        if (G && s < kDmaPerWave) gather_copy(gbase, go, s);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -466,15 +474,20 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
       if (ntiles > 2) wait_vmem<kDmaPerWave>();
       else wait_vmem<0>();
       __syncthreads();   // tile 0 scored, tile 1 landed
-      for (int j = 0; j + 1 < ntiles; ++j) {
-        // the gather of tile j+3 goes into the stage of tile j-1, which every
-        // wave left at the last barrier
-        pv_tile(j, j + 3 < ntiles ? j + 3 : -1);
-        if (j + 3 < ntiles) wait_vmem<kDmaPerWave>();   // tile j+2 landed; tile j+3 may still fly
-        else wait_vmem<0>();
+      // the gather of tile j+3 goes into the stage of tile j-1, which every
+      // wave left at the last barrier
+      int j = 0;
+      for (; j + 3 < ntiles; ++j) {
+        pv_tile(std::true_type{}, j, j + 3);
+        wait_vmem<kDmaPerWave>();   // tile j+2 landed; tile j+3 may still fly
         __syncthreads();
       }
-      pv_tile(ntiles - 1, -1);
+      for (; j + 1 < ntiles; ++j) {
+        pv_tile(std::false_type{}, j, -1);
+        wait_vmem<0>();
+        __syncthreads();
+      }
+      pv_tile(std::false_type{}, ntiles - 1, -1);
     }
 
     // ---------------------------------------------------------------- 6. epilogue (O)
