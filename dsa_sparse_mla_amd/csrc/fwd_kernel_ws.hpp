@@ -100,15 +100,7 @@ __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
 __device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
-// max / sum over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48)
-__device__ __forceinline__ float max_kgroups(float x) {
-  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-  swap16(a, b);   // a: rows (0,0,2,2), b: rows (1,1,3,3)
-  x = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-  a = __builtin_bit_cast(uint32_t, x), b = a;
-  swap32(a, b);   // a: halves (0,0), b: halves (1,1)
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-}
+// sum over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48)
 __device__ __forceinline__ float sum_kgroups(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
   swap16(a, b);
@@ -219,7 +211,7 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
     };
 
     // per head tile ht (head 32hh + 16ht + hcol): reference, row sum of the
-    // settled tiles, and the last scored tile's scaled scores (keys
+    // settled tiles, and the last scored tile's raw scores q.k (keys
     // 16kd + kq_key .. +3, masked = -inf) with their numerator sum
     float m_ref[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.f, 0.f};
@@ -233,11 +225,18 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
     // numerators of the scored tile t under the current references -> P buffer
     auto make_p = [&](int t) {
       const uint32_t pb = p_of(t);
+      const bool partial = (t + 1) * kTileKeys > nvalid;   // uniform
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[ht][i] - m_ref[ht]);
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[ht][i], a.scale_log2, -m_ref[ht]));
+        if (partial) {   // a masked slot has weight 0, also when the scale is 0
+          const int key0 = t * kTileKeys + 16 * kd + kq_key;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (key0 + i >= nvalid) p[i] = 0.f;
+        }
         psum[ht] = (p[0] + p[1]) + (p[2] + p[3]);
         const u32x2_t w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
         lds_write_b64_at(pb + p_off(32 * hh + 16 * ht + hcol, (16 * kd + kq_key) >> 3) + 2 * (kq_key & 7), w);
@@ -285,20 +284,30 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
                                                               c == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : sacc[t & 1], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // raw scores, masked = -inf (the scale >= 0 is applied to maxima and
+      // inside the exponent only)
       const bool partial = (ts + 1) * kTileKeys > nvalid;   // uniform
       const int key0 = ts * kTileKeys + 16 * kd + kq_key;
+      auto scaled = [&](float x) { return x == -INFINITY ? -INFINITY : x * a.scale_log2; };   // the scale may be 0
       bool exceed = false;
+      float ml[2];
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = sacc[ht][i] * a.scale_log2;
-          sv[ht][i] = partial && key0 + i >= nvalid ? -INFINITY : x;
-        }
-        const float ml = fmaxf(fmaxf(sv[ht][0], sv[ht][1]), fmaxf(sv[ht][2], sv[ht][3]));
-        exceed = exceed || ml > m_ref[ht] + kWsSlack;
-        const float mx = max_kgroups(ml);
-        if (kq == 0) s_mx[ts & 1][kd][32 * hh + 16 * ht + hcol] = mx;
+        for (int i = 0; i < 4; ++i) sv[ht][i] = partial && key0 + i >= nvalid ? -INFINITY : sacc[ht][i];
+        ml[ht] = fmaxf(fmaxf(sv[ht][0], sv[ht][1]), fmaxf(sv[ht][2], sv[ht][3]));
+        exceed = exceed || scaled(ml[ht]) > m_ref[ht] + kWsSlack;
+      }
+      // block maxima of both head tiles in two lane swaps: after them rows
+      // 0 and 2 (kq even) hold head tile 0's maximum, rows 1 and 3 tile 1's
+      {
+        uint32_t x0 = __builtin_bit_cast(uint32_t, ml[0]), x1 = __builtin_bit_cast(uint32_t, ml[1]);
+        swap16(x0, x1);   // x0: rows (t0 r0, t1 r0, t0 r2, t1 r2), x1: (t0 r1, t1 r1, t0 r3, t1 r3)
+        uint32_t y0 = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, x0), __builtin_bit_cast(float, x1)));
+        uint32_t y1 = y0;
+        swap32(y0, y1);   // y0: low half twice, y1: high half twice
+        const float mx = fmaxf(__builtin_bit_cast(float, y0), __builtin_bit_cast(float, y1));
+        if (kq < 2) s_mx[ts & 1][kd][32 * hh + 16 * kq + hcol] = scaled(mx);
       }
       const bool any = __ballot(exceed) != 0;
       if (lane == 0) s_flag[ts & 1][sw] = any ? 1 : 0;
