@@ -214,6 +214,13 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
     // settled tiles, and the last scored tile's raw scores q.k (keys
     // 16kd + kq_key .. +3, masked = -inf) with their numerator sum
     float m_ref[2] = {-INFINITY, -INFINITY};
+    // A raw score q.k above thr flags its tile: in log2 units it exceeds the
+    // reference by more than kWsSlack (with scale 0 every score is 0).
+    auto raw_threshold = [&](float m) {
+      const float t = m + kWsSlack;
+      return a.scale_log2 > 0.f ? t / a.scale_log2 : (t < 0.f ? -INFINITY : INFINITY);
+    };
+    float thr[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.f, 0.f};
     float sv[2][4];
     float psum[2] = {0.f, 0.f};
@@ -252,6 +259,7 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
           const float mn = next_ref(m_ref[ht], fmaxf(s_mx[b][0][h], s_mx[b][1][h]));
           const float al = ref_factor(m_ref[ht], mn);
           m_ref[ht] = mn;
+          thr[ht] = raw_threshold(mn);
           l_run[ht] *= al;
           if (kd == 0 && kq == 0) s_alpha[h] = al;
         }
@@ -296,7 +304,7 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[ht][i] = partial && key0 + i >= nvalid ? -INFINITY : sacc[ht][i];
         ml[ht] = fmaxf(fmaxf(sv[ht][0], sv[ht][1]), fmaxf(sv[ht][2], sv[ht][3]));
-        exceed = exceed || scaled(ml[ht]) > m_ref[ht] + kWsSlack;
+        exceed = exceed || ml[ht] > thr[ht];
       }
       // block maxima of both head tiles in two lane swaps: after them rows
       // 0 and 2 (kq even) hold head tile 0's maximum, rows 1 and 3 tile 1's
@@ -307,7 +315,7 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
         uint32_t y1 = y0;
         swap32(y0, y1);   // y0: low half twice, y1: high half twice
         const float mx = fmaxf(__builtin_bit_cast(float, y0), __builtin_bit_cast(float, y1));
-        if (kq < 2) s_mx[ts & 1][kd][32 * hh + 16 * kq + hcol] = scaled(mx);
+        s_mx[ts & 1][kd][32 * hh + 16 * (kq & 1) + hcol] = scaled(mx);   // rows 2, 3 repeat rows 0, 1
       }
       const bool any = __ballot(exceed) != 0;
       if (lane == 0) s_flag[ts & 1][sw] = any ? 1 : 0;
