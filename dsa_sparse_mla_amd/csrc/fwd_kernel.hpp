@@ -348,24 +348,33 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
   const uint32_t stage_lds = lds_offset(s_stage);
   // Per-lane LDS bases (inside a stage); every operand address is one of them
   // plus a compile-time offset.
-  // S operand, dims 32c + 8kq .. +7 of row 16b + hcol. Latent (c < 16):
+  // Key order inside a 16-key block: MFMA row i (lane i & 15 of the K
+  // operand) is key kr = 4 sigma(i >> 2) + (i & 3), so S^T row 4q + e and P^T
+  // slot e of k-group q hold key 4 sigma(q) + e. A ds_read_b128 serves in one
+  // cycle the 16 lanes of a half-wave whose quad index (lane bits 2..4) has
+  // one parity; with sigma = (1, 0, 2, 3) and swz those lanes hit 16 distinct
+  // slots (with the identity, every latent K read is a 2-way conflict).
+  const int ksig = 4 * ((0x3201 >> (4 * kq)) & 15);   // 4 sigma(kq): first key of this lane's k-group
+  const int kr = 4 * ((0x3201 >> (4 * (hcol >> 2))) & 15) + (hcol & 3);
+  // S operand, dims 32c + 8kq .. +7 of row 16b + kr. Latent (c < 16):
   // granule (4c + kq) ^ fh = 4 * ((c & ~3) + ((c & 3) ^ (fh >> 2))) + (kq ^ (fh & 3)),
-  // fh = swz(hcol) = swz(16b + hcol).
-  const int fh = swz(hcol);
+  // fh = swz(kr) = swz(16b + kr).
+  const int fh = swz(kr);
   int kbase[4];
 #pragma unroll
   for (int cl = 0; cl < 4; ++cl)
-    kbase[cl] = hcol * 1024 + 16 * (4 * (cl ^ (fh >> 2)) + (kq ^ (fh & 3)));
-  // rope (c = 16, 17): granule (4(c-16) + kq) ^ ((hcol >> 1) & 7) of a 128 B row
+    kbase[cl] = kr * 1024 + 16 * (4 * (cl ^ (fh >> 2)) + (kq ^ (fh & 3)));
+  // rope (c = 16, 17): granule (4(c-16) + kq) ^ ((kr >> 1) & 7) of a 128 B row
   int rbase[2];
 #pragma unroll
-  for (int cr = 0; cr < 2; ++cr) rbase[cr] = kRopeOff + hcol * 128 + 16 * ((4 * cr + kq) ^ ((hcol >> 1) & 7));
+  for (int cr = 0; cr < 2; ++cr) rbase[cr] = kRopeOff + kr * 128 + 16 * ((4 * cr + kq) ^ ((kr >> 1) & 7));
   // V operand (transposed): rows vr (slots 0-3) and 16 + vr (slots 4-7),
   // columns dv0 + 16jt + 4(hcol & 3) .. +3, i.e. granule
   // dv0/8 + 2jt + ((hcol >> 1) & 1) at byte (hcol & 1) * 8; both rows have
   // swizzle swz(vr), so the stored granule is
-  // dv0/8 + 16(jt >> 3) + ((2(jt & 7) + gl) ^ swz(vr)).
-  const int vr = 4 * kq + (hcol >> 2);
+  // dv0/8 + 16(jt >> 3) + ((2(jt & 7) + gl) ^ swz(vr)). The 16 lanes of
+  // k-group kq read keys ksig .. ksig+3, the keys of their P^T slots.
+  const int vr = ksig + (hcol >> 2);
   const int fv = swz(vr);
   int vbase[8];
 #pragma unroll
@@ -401,7 +410,7 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
   float alpha = 1.f;
 
   // Slice k of the softmax of tile jn. sacc[b][i] = raw score q . k of key
-  // 32jn + 16b + 4kq + i for head `head`; the scale (>= 0, folded with
+  // 32jn + 16b + ksig + i for head `head`; the scale (>= 0, folded with
   // log2 e) is applied inside the exponent.
   auto soft_piece = [&](int k, int jn) {
     if (k == 0) {
@@ -410,7 +419,7 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sp[b][i] = sacc[b][i];
       if ((jn + 1) * kTileKeys > nvalid) {   // the last tile: mask keys past the list
-        const int kb = jn * kTileKeys + 4 * kq;
+        const int kb = jn * kTileKeys + ksig;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -438,7 +447,7 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sp[b][i] = fast_exp2(__builtin_fmaf(sp[b][i], a.scale_log2, -m_run));
       if ((jn + 1) * kTileKeys > nvalid) {   // last tile: a masked slot has weight 0 (also when the scale is 0)
-        const int kb = jn * kTileKeys + 4 * kq + 16 * b;
+        const int kb = jn * kTileKeys + ksig + 16 * b;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (kb + i >= nvalid) sp[b][i] = 0.f;
