@@ -192,6 +192,9 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 skips it)")
+    ap.add_argument("--flush", action="store_true",
+                    help="also time launches with a 512 MB scratch write between them (caches cold), "
+                         "reported as kernel_ms_flushed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a copy of known size (for HBM counter scaling)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -266,6 +269,25 @@ def main():
     med_ms = per_launch_ms[len(per_launch_ms) // 2]
     ms_per_step = wall * 1e3 / args.steps
 
+    flushed_ms = None
+    if args.flush:
+        # L2 and MALL hold no KV when each launch starts: a 512 MB write
+        # between launches, outside the events
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        fl = []
+        for i in range(args.steps):
+            scratch.fill_(i & 255)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            fl.append(e0.elapsed_time(e1))
+        fl.sort()
+        flushed_ms = fl[len(fl) // 2]
+        del scratch
+
     gbps = gathered / (ms_per_step * 1e-3) / 1e9
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     kern_gbps = gathered / (avg_ms * 1e-3) / 1e9
@@ -303,6 +325,9 @@ def main():
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 3),
         "roofline": roof,
+        **({"kernel_ms_flushed": round(flushed_ms, 5),
+            "gathered_kv_gbps_flushed": round(gathered / (flushed_ms * 1e-3) / 1e9, 2)}
+           if flushed_ms is not None else {}),
         "source_hash": source_hash(),
     }
     if args.cpu_budget > 0:
