@@ -203,6 +203,7 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
     //   (kb0 ^ 64(c & 3)) + 256(c >> 2);  rope chunk 16 + cr: rb0 ^ 64cr
     const int kr_row = 16 * kd + key_rho(hcol);
     const int kq_key = 4 * key_sigma(kq);   // this lane's scores: keys 16kd + kq_key .. +3
+    const int kpos = 16 * kd + kq_key;      // ... at positions kpos .. +3 of the tile
     const uint32_t kb0 = kr_row * 1024 + 16 * (kq ^ swz_ws(kr_row));
     const uint32_t rb0 = kRopeOff + kr_row * 128 + 16 * (kq ^ ((kr_row >> 1) & 7));
     auto kread = [&](uint32_t st, int c) {
@@ -214,11 +215,15 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
     // settled tiles, and the last scored tile's raw scores q.k (keys
     // 16kd + kq_key .. +3, masked = -inf) with their numerator sum
     float m_ref[2] = {-INFINITY, -INFINITY};
+    // Scale used here: a zero scale becomes 1e-30, which leaves every weight
+    // 2^(s * 1e-30 - m) equal to 1 in fp32 but keeps -inf * scale = -inf, so a
+    // masked score (-inf) gives weight 0 without a separate mask.
+    const float sc = fmaxf(a.scale_log2, 1e-30f);
     // A raw score q.k above thr flags its tile: in log2 units it exceeds the
     // reference by more than kWsSlack (with scale 0 every score is 0).
     auto raw_threshold = [&](float m) {
       const float t = m + kWsSlack;
-      return a.scale_log2 > 0.f ? t / a.scale_log2 : (t < 0.f ? -INFINITY : INFINITY);
+      return t / sc;
     };
     float thr[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.f, 0.f};
@@ -232,18 +237,11 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
     // numerators of the scored tile t under the current references -> P buffer
     auto make_p = [&](int t) {
       const uint32_t pb = p_of(t);
-      const bool partial = (t + 1) * kTileKeys > nvalid;   // uniform
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[ht][i], a.scale_log2, -m_ref[ht]));
-        if (partial) {   // a masked slot has weight 0, also when the scale is 0
-          const int key0 = t * kTileKeys + 16 * kd + kq_key;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (key0 + i >= nvalid) p[i] = 0.f;
-        }
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[ht][i], sc, -m_ref[ht]));   // masked: 0
         psum[ht] = (p[0] + p[1]) + (p[2] + p[3]);
         const u32x2_t w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
         lds_write_b64_at(pb + p_off(32 * hh + 16 * ht + hcol, (16 * kd + kq_key) >> 3) + 2 * (kq_key & 7), w);
@@ -294,15 +292,14 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
       }
       // raw scores, masked = -inf (the scale >= 0 is applied to maxima and
       // inside the exponent only)
-      const bool partial = (ts + 1) * kTileKeys > nvalid;   // uniform
-      const int key0 = ts * kTileKeys + 16 * kd + kq_key;
-      auto scaled = [&](float x) { return x == -INFINITY ? -INFINITY : x * a.scale_log2; };   // the scale may be 0
+      const int lim = nvalid - ts * kTileKeys;   // keys of this tile in the list (>= 32 unless it is the last)
+      auto scaled = [&](float x) { return x * sc; };
       bool exceed = false;
       float ml[2];
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[ht][i] = partial && key0 + i >= nvalid ? -INFINITY : sacc[ht][i];
+        for (int i = 0; i < 4; ++i) sv[ht][i] = kpos + i >= lim ? -INFINITY : sacc[ht][i];
         ml[ht] = fmaxf(fmaxf(sv[ht][0], sv[ht][1]), fmaxf(sv[ht][2], sv[ht][3]));
         exceed = exceed || ml[ht] > thr[ht];
       }
