@@ -242,6 +242,47 @@ def test_paged_wide_heads():
     check(np32(out), np32(lse), ro, rl, "paged H=64")
 
 
+@pytest.mark.parametrize("H,T,splits", [(64, 3000, 1), (128, 1500, 1), (64, 1500, 2)])
+def test_many_mixed_rows(H, T, splits):
+    """About 3000 (token, split, head block) workgroups of the 64-head kernel
+    (several per CU, so later ones start while others run) with row lengths
+    from 0 to 8 tiles shuffled among -1 and junk values: empty rows, rows of
+    1-3 tiles and longer ones side by side. Repeated runs are bitwise equal."""
+    N, topk = 4096, 256
+    g = torch.Generator().manual_seed(40 + H + splits)
+    rng = np.random.default_rng(40 + H + splits)
+    q = torch.randn((T, H, 576), generator=g).to(torch.bfloat16)
+    kv = torch.randn((N, 576), generator=g).to(torch.bfloat16)
+    idx = np.full((T, topk), -1, dtype=np.int32)
+    nvalid = rng.integers(0, topk + 1, size=T)
+    nvalid[rng.random(T) < 0.05] = 0
+    for t in range(T):
+        row = idx[t]
+        row[:nvalid[t]] = rng.integers(0, N, size=nvalid[t])
+        row[nvalid[t]:] = rng.choice(np.array([-1, -1, -1, N, -5], dtype=np.int32), size=topk - nvalid[t])
+        rng.shuffle(row)
+    idx = torch.from_numpy(idx)
+    out, lse = run_flat(q, kv, idx, 1 / 24, num_splits=splits)
+    check(np32(out), np32(lse), *ref_flat(q, kv, idx, 1 / 24), f"mixed H={H} T={T} splits={splits}")
+    out2, lse2 = run_flat(q, kv, idx, 1 / 24, num_splits=splits)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_paged_many_mixed_rows():
+    """The paged 64-head kernel over 1800 query tokens of 300 short sequences
+    (contexts of 40-700 tokens, so many rows hold fewer than topk entries)."""
+    d = workloads.make_paged(num_seqs=300, q_per_seq=6, num_heads=64, min_len=40, max_len=700, topk=128)
+    dev = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in d.items()}
+    out, lse = _dsa().sparse_mla_fwd_paged(dev["q"], dev["kv_pages"], dev["page_table"],
+                                           dev["seq_lens"], dev["indices"], d["sm_scale"],
+                                           d["q_per_seq"])
+    torch.cuda.synchronize()
+    ro, rl = sparse_mla_fwd_paged_ref(np32(d["q"]), np32(d["kv_pages"]), d["page_table"].numpy(),
+                                      d["seq_lens"].numpy(), d["indices"].numpy(), d["sm_scale"],
+                                      d["q_per_seq"])
+    check(np32(out), np32(lse), ro, rl, "paged mixed H=64")
+
+
 def test_strided_inputs_and_outputs():
     T, H, N, k = 12, 8, 700, 200
     q_big, kv, idx = random_case(T=T, H=H * 2, N=N, topk=k, seed=13)
