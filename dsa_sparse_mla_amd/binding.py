@@ -66,6 +66,18 @@ def lib() -> ctypes.CDLL:
             vp, i64,                 # lse
             i32, vp, i64,            # num_splits, workspace, bytes
             vp]                      # stream
+        L.dsa_sparse_mla_bwd.restype = ctypes.c_int
+        L.dsa_sparse_mla_bwd.argtypes = [
+            vp, i64, i64,            # q
+            vp, i64, i64,            # kv, row stride, num_kv
+            vp, i64,                 # indices
+            i64, i32, i32, f32,      # T, H, topk, sm_scale
+            vp, i64, i64,            # out (forward output)
+            vp, i64,                 # lse (forward LSE)
+            vp, i64, i64,            # dout
+            vp, i64, i64,            # dq
+            vp, i64,                 # dkv, row stride
+            vp]                      # stream
         L.dsa_sparse_mla_workspace_size.restype = ctypes.c_int
         L.dsa_sparse_mla_workspace_size.argtypes = [i64, i32, i32, i32,
                                                     ctypes.POINTER(i32), ctypes.POINTER(i64)]
@@ -198,3 +210,52 @@ def sparse_mla_fwd_paged(q, kv_pages, page_table, seq_lens, indices, sm_scale, q
     if st != 0:
         raise DsaError(st, "dsa_sparse_mla_fwd_paged")
     return out, lse
+
+
+def sparse_mla_bwd(q, kv, indices, sm_scale, out, lse, dout, dq=None, dkv=None):
+    """Sparse MLA backward over flat KV: gradients of the forward output.
+
+    q [T,H,576] bf16, kv [N,576] bf16, indices [T,topk] int32 as in the
+    forward; out [T,H,512] bf16 and lse [T,H] fp32 from the forward on these
+    inputs; dout [T,H,512] bf16. Returns (dq [T,H,576] fp32, dkv [N,576] fp32);
+    dkv is written in full (rows no index names are 0).
+    """
+    dev = q.device
+    _check(q, "q", torch.bfloat16, 3, dev)
+    _check(kv, "kv", torch.bfloat16, 2, dev)
+    _check(indices, "indices", torch.int32, 2, dev)
+    _check(dout, "dout", torch.bfloat16, 3, dev)
+    T, H, D = q.shape
+    N = kv.shape[0]
+    if D != DQK or kv.shape[1] != DQK:
+        raise ValueError("q and kv rows must be 576 wide")
+    if indices.shape[0] != T or tuple(dout.shape) != (T, H, DV):
+        raise ValueError("indices need one row per token and dout the shape of out")
+    _check(out, "out", torch.bfloat16, 3, dev)
+    _check(lse, "lse", torch.float32, 2, dev)
+    if tuple(out.shape) != (T, H, DV) or tuple(lse.shape) != (T, H):
+        raise ValueError("out must be [T, H, 512] and lse [T, H]")
+    if dq is None:
+        dq = torch.empty((T, H, DQK), dtype=torch.float32, device=dev)
+    if dkv is None:
+        dkv = torch.empty((N, DQK), dtype=torch.float32, device=dev)
+    _check(dq, "dq", torch.float32, 3, dev)
+    _check(dkv, "dkv", torch.float32, 2, dev)
+    if tuple(dq.shape) != (T, H, DQK) or tuple(dkv.shape) != (N, DQK):
+        raise ValueError("dq must be [T, H, 576] and dkv [N, 576]")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib().dsa_sparse_mla_bwd(
+            q.data_ptr(), q.stride(0), q.stride(1),
+            kv.data_ptr(), kv.stride(0), N,
+            indices.data_ptr(), indices.stride(0),
+            T, H, indices.shape[1], float(sm_scale),
+            out.data_ptr(), out.stride(0), out.stride(1),
+            lse.data_ptr(), lse.stride(0),
+            dout.data_ptr(), dout.stride(0), dout.stride(1),
+            dq.data_ptr(), dq.stride(0), dq.stride(1),
+            dkv.data_ptr(), dkv.stride(0),
+            stream)
+    if st != 0:
+        raise DsaError(st, "dsa_sparse_mla_bwd")
+    return dq, dkv

@@ -1,0 +1,288 @@
+// Backward of the DSA sparse MLA forward for gfx950 (MI355X): gradients with
+// respect to q and kv, given the upstream gradient dO, the forward output O
+// and the forward LSE.
+//
+// With J the valid entries of token t's index row, K = kv[J] (|J| x 576),
+// V = K[:, :512], s = sm_scale, and per head h:
+//   P   = exp(s q.K^T - LSE)          (the forward's softmax, from its LSE)
+//   dP  = dO V^T,   D = dO . O,   dS = P (dP - D)
+//   dq        = s dS K
+//   dkv[J]   += s dS^T q              (all 576 columns: the key use)
+//   dkv[J,:512] += P^T dO             (the value use)
+// Entries that name no row get nothing; duplicates count once per occurrence.
+//
+// One workgroup of 4 waves handles one token and a block of 16 heads. The
+// index row is compacted per 2048-entry segment, as in the forward. Per tile
+// of 32 keys:
+//   phase 1: waves 0,1: S^T = K Q^T on key block 0 / 1 (16x16x32 MFMA, Q^T
+//            in registers); waves 2,3: dP^T = V dO^T likewise (dO^T in
+//            registers), handed to waves 0,1 through LDS;
+//   phase 2: waves 0,1: P and s*dS in bf16 into LDS, [head][32 keys];
+//   phase 3: every wave: dq (9 of the 36 16-column tiles) += (s dS) K, with
+//            K^T read transposed from the tile (ds_read_b64_tr_b16); and
+//            dkv tiles [16 keys x 16 columns] = (s dS)^T Q + P^T dO on
+//            16x16x16 MFMA over the 16 heads, added to the caller's fp32
+//            dkv with atomics (other tokens name the same rows).
+// The next tile's rows are loaded into registers while the current one is
+// processed and stored to the other LDS stage at its end.
+//
+// Pages: "[Feature] Add optional FlashMLA backend for DSA Sparse MLA"
+// (xtuner PR 2083), Motivation (forward output and LSE feed the backward);
+// the prime-rl pull request 4078 that adds a `cudnn_flashmla` DSA backend
+// (a separate DSA backward kernel, timed per call).
+#pragma once
+
+#include "fwd_kernel.hpp"
+
+namespace dsa {
+
+struct BwdArgs {
+  const uint16_t* q;       // bf16 [T, H, 576]
+  int64_t q_st, q_sh;
+  const uint16_t* kv;      // bf16 [N, 576]
+  int64_t kv_st;           // row stride in elements
+  int64_t num_kv;
+  const int32_t* idx;      // int32 [T, topk]
+  int64_t idx_st;
+  int64_t num_tokens;
+  int32_t num_heads;
+  int32_t topk;
+  float scale;             // sm_scale
+  float scale_log2;        // sm_scale * log2(e)
+  const uint16_t* out;     // bf16 [T, H, 512], the forward output
+  int64_t o_st, o_sh;
+  const float* lse;        // fp32 [T, H], the forward LSE (natural log)
+  int64_t lse_st;
+  const uint16_t* dout;    // bf16 [T, H, 512]
+  int64_t do_st, do_sh;
+  float* dq;               // fp32 [T, H, 576]
+  int64_t dq_st, dq_sh;
+  float* dkv;              // fp32 [N, 576], zeroed before this kernel
+  int64_t dkv_st;
+  int32_t head_blocks;     // workgroups per token (16 heads each)
+};
+
+constexpr int kBwHeads = 16;
+constexpr int kBwPitch = 1168;                  // LDS row pitch of K rows and Q rows: 1152 + 16
+constexpr int kBwStage = kTileKeys * kBwPitch;  // one tile of 32 rows
+constexpr int kBwOPitch = 1040;                 // LDS row pitch of dO rows: 1024 + 16
+constexpr int kBwGran = kTileKeys * (kDqk / 8) / 256;   // 16-byte granules per thread per tile (9)
+static_assert(kTileKeys * (kDqk / 8) % 256 == 0, "a tile splits evenly over the threads");
+
+__device__ __forceinline__ bf16x8_t lds16(const uint8_t* p) { return *(const bf16x8_t*)p; }
+
+__global__ void __launch_bounds__(256)
+sparse_mla_bwd_kernel(const BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[2][kBwStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[kBwHeads * kBwPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t s_do[kBwHeads * kBwOPitch];
+  __shared__ __attribute__((aligned(16))) float4_t s_dp[2][64];          // dP^T of key block 0 / 1
+  __shared__ __attribute__((aligned(16))) uint8_t s_pt[kBwHeads * 64];   // P, bf16 [head][32 keys]
+  __shared__ __attribute__((aligned(16))) uint8_t s_dst[kBwHeads * 64];  // s*dS, bf16 [head][32 keys]
+  __shared__ __attribute__((aligned(16))) uint32_t s_rows[kSegment];     // compacted row ids
+  __shared__ int s_cnt[kChunks];
+  __shared__ float s_D[kBwHeads], s_lse2[kBwHeads];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;   // MFMA column / k-group of the lane
+  const int64_t token = blockIdx.x / a.head_blocks;
+  const int h0 = (int)(blockIdx.x % a.head_blocks) * kBwHeads;
+
+  // ---------------------------------------------------------------- per-token inputs
+  // Q (16 x 576) and dO (16 x 512) of the head block into LDS; padded heads are 0.
+  for (int i = tid; i < kBwHeads * (kDqk / 8); i += 256) {
+    const int h = i / (kDqk / 8), c = i % (kDqk / 8);
+    bf16x8_t v = {};
+    if (h0 + h < a.num_heads) v = *(const bf16x8_t*)(a.q + token * a.q_st + (int64_t)(h0 + h) * a.q_sh + 8 * c);
+    *(bf16x8_t*)(s_q + h * kBwPitch + 16 * c) = v;
+  }
+  for (int i = tid; i < kBwHeads * (kDv / 8); i += 256) {
+    const int h = i / (kDv / 8), c = i % (kDv / 8);
+    bf16x8_t v = {};
+    if (h0 + h < a.num_heads) v = *(const bf16x8_t*)(a.dout + token * a.do_st + (int64_t)(h0 + h) * a.do_sh + 8 * c);
+    *(bf16x8_t*)(s_do + h * kBwOPitch + 16 * c) = v;
+  }
+  // D = dO . O and LSE (log2 units) per head: wave w takes heads 4w .. 4w+3
+  for (int hh = 0; hh < 4; ++hh) {
+    const int h = 4 * wave + hh;
+    float d = 0.f;
+    if (h0 + h < a.num_heads) {
+      const bf16x8_t o = *(const bf16x8_t*)(a.out + token * a.o_st + (int64_t)(h0 + h) * a.o_sh + 8 * lane);
+      const bf16x8_t dd = *(const bf16x8_t*)(a.dout + token * a.do_st + (int64_t)(h0 + h) * a.do_sh + 8 * lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d += (float)o[e] * (float)dd[e];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) d += __shfl_xor(d, off);
+    if (lane == 0) {
+      s_D[h] = d;
+      // padded heads: +inf, so their P = exp2(score - inf) = 0
+      s_lse2[h] = h0 + h < a.num_heads ? a.lse[token * a.lse_st + h0 + h] * 1.4426950408889634f : INFINITY;
+    }
+  }
+  __syncthreads();
+
+  // Q^T (waves 0, 1) or dO^T (waves 2, 3) as the MFMA B operand: lane holds
+  // head n, columns 32c + 8g .. +7
+  const bool s_role = wave < 2;
+  const int kb = wave & 1;   // key block of the phase-1 product
+  bf16x8_t breg[kDqk / 32];
+#pragma unroll
+  for (int c = 0; c < kDqk / 32; ++c)
+    breg[c] = s_role ? lds16(s_q + n * kBwPitch + 2 * (32 * c + 8 * g))
+                     : (c < kDv / 32 ? lds16(s_do + n * kBwOPitch + 2 * (32 * c + 8 * g)) : (bf16x8_t){});
+
+  float4_t dq_acc[9];   // dq tiles 9w .. 9w+8: lane holds column 16dt + n of heads 4g .. 4g+3
+#pragma unroll
+  for (int k = 0; k < 9; ++k) dq_acc[k] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  FwdArgs fa = {};   // the forward's index stage, with row ids as the offsets
+  fa.idx = a.idx;
+  fa.idx_st = a.idx_st;
+  fa.num_kv = a.num_kv;
+  fa.kv_row_gran = 1;
+  fa.topk = a.topk;
+  fa.seg_len = kSegment;
+
+  const int nseg = (a.topk + kSegment - 1) / kSegment;
+  for (int seg = 0; seg < nseg; ++seg) {
+    const int nvalid = build_key_list<false>(fa, token, seg, wave, lane, s_rows, s_cnt, [] {});
+    const int ntiles = (nvalid + kTileKeys - 1) / kTileKeys;
+
+    // rows of tile t: thread tid holds granules tid + 256k (row = gi / 72, granule gi % 72)
+    bf16x8_t greg[kBwGran];
+    auto load_tile = [&](int t) {
+#pragma unroll
+      for (int k = 0; k < kBwGran; ++k) {
+        const int gi = tid + 256 * k, row = gi / (kDqk / 8), c = gi % (kDqk / 8);
+        const uint32_t rid = s_rows[t * kTileKeys + row];
+        greg[k] = *(const bf16x8_t*)(a.kv + (int64_t)rid * a.kv_st + 8 * c);
+      }
+    };
+    auto store_tile = [&](int t) {
+      uint8_t* st = s_stage[t & 1];
+#pragma unroll
+      for (int k = 0; k < kBwGran; ++k) {
+        const int gi = tid + 256 * k, row = gi / (kDqk / 8), c = gi % (kDqk / 8);
+        *(bf16x8_t*)(st + row * kBwPitch + 16 * c) = greg[k];
+      }
+    };
+    if (ntiles > 0) {
+      load_tile(0);
+      store_tile(0);
+    }
+    __syncthreads();
+
+    for (int j = 0; j < ntiles; ++j) {
+      if (j + 1 < ntiles) load_tile(j + 1);   // in flight during the three phases
+      const uint8_t* st = s_stage[j & 1];
+
+      // ---- phase 1: S^T (waves 0, 1) or dP^T (waves 2, 3) of key block kb
+      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* arow = st + (kb * 16 + n) * kBwPitch + 16 * g;   // key kb*16 + n, columns 8g ..
+      if (s_role) {
+#pragma unroll
+        for (int c = 0; c < kDqk / 32; ++c)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow + 64 * c), breg[c], acc, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int c = 0; c < kDv / 32; ++c)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow + 64 * c), breg[c], acc, 0, 0, 0);
+        s_dp[kb][lane] = acc;
+      }
+      __syncthreads();
+
+      // ---- phase 2: P and s*dS (lane: head n, keys kb*16 + 4g + e)
+      if (s_role) {
+        const float4_t dp = s_dp[kb][lane];
+        const float Dh = s_D[n], l2 = s_lse2[n];
+        const int lim = nvalid - j * kTileKeys;
+        float p[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = kb * 16 + 4 * g + e < lim;
+          p[e] = ok ? __builtin_amdgcn_exp2f(acc[e] * a.scale_log2 - l2) : 0.f;
+          ds[e] = p[e] * (dp[e] - Dh) * a.scale;
+        }
+        const int off = n * 64 + 2 * (kb * 16 + 4 * g);
+        *(uint2*)(s_pt + off) = (uint2){pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+        *(uint2*)(s_dst + off) = (uint2){pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
+      }
+      __syncthreads();
+
+      // ---- phase 3a: dq tiles 9w .. 9w+8 += (s dS)[16 heads x 32 keys] K[32 keys x 16 columns]
+      {
+        const bf16x8_t ads = lds16(s_dst + n * 64 + 16 * g);   // head n, keys 8g .. 8g+7
+        // K^T operand: lane (g, n) points at key 8g + 4half + n/4, columns d0 + 4(n % 4)
+        const uint8_t* kt = st + (8 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
+#pragma unroll
+        for (int k = 0; k < 9; ++k) {
+          const int d0 = 16 * (9 * wave + k);
+          const short4_t lo = lds_read_tr16(kt + 2 * d0);
+          const short4_t hi = lds_read_tr16(kt + 4 * kBwPitch + 2 * d0);
+          const bf16x8_t b = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          dq_acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads, b, dq_acc[k], 0, 0, 0);
+        }
+      }
+      // ---- phase 3b: dkv of key block kb2 = w >> 1, column tiles 18(w & 1) .. +17:
+      //   [16 keys x 16 columns] = (s dS)^T Q + P^T dO over the 16 heads
+      {
+        const int kb2 = wave >> 1;
+        // A operands: lane (g, n) points at head 4g + n/4, keys kb2*16 + 4(n % 4);
+        // it receives key kb2*16 + n of heads 4g .. 4g+3
+        const int aoff = (4 * g + (n >> 2)) * 64 + 2 * (kb2 * 16 + 4 * (n & 3));
+        const short4_t ads = lds_read_tr16(s_dst + aoff);
+        const short4_t ap = lds_read_tr16(s_pt + aoff);
+        // B operands: lane (g, n) points at head 4g + n/4, columns d0 + 4(n % 4)
+        const uint8_t* bq = s_q + (4 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
+        const uint8_t* bo = s_do + (4 * g + (n >> 2)) * kBwOPitch + 8 * (n & 3);
+        // this lane's outputs: column d0 + n of keys kb2*16 + 4g + e
+        const int kbase = j * kTileKeys + kb2 * 16 + 4 * g;
+        uint32_t rid[4];
+        bool rok[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          rid[e] = s_rows[kbase + e];
+          rok[e] = kbase + e < nvalid;
+        }
+#pragma unroll 2
+        for (int k = 0; k < 18; ++k) {
+          const int d0 = 16 * (18 * (wave & 1) + k);
+          float4_t c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ads, lds_read_tr16(bq + 2 * d0),
+                                                                 (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          if (d0 < kDv) c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap, lds_read_tr16(bo + 2 * d0), c, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (rok[e]) unsafeAtomicAdd(a.dkv + (int64_t)rid[e] * a.dkv_st + d0 + n, c[e]);
+        }
+      }
+      if (j + 1 < ntiles) store_tile(j + 1);   // the other stage: last read before this tile's barrier
+      __syncthreads();
+    }
+  }
+
+  // ---------------------------------------------------------------- dq (fp32)
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    const int d = 16 * (9 * wave + k) + n;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int h = h0 + 4 * g + e;
+      if (h < a.num_heads) a.dq[token * a.dq_st + (int64_t)h * a.dq_sh + d] = dq_acc[k][e];
+    }
+  }
+}
+
+// dkv = 0 before the backward accumulates into it: one thread per float4.
+__global__ void __launch_bounds__(256)
+dkv_zero_kernel(float* dkv, int64_t rows, int64_t row_stride) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_row = kDqk / 4;
+  if (i >= rows * per_row) return;
+  const int64_t r = i / per_row, c = i % per_row;
+  *(float4_t*)(dkv + r * row_stride + 4 * c) = (float4_t){0.f, 0.f, 0.f, 0.f};
+}
+
+}  // namespace dsa

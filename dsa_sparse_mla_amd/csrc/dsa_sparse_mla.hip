@@ -14,6 +14,7 @@
 #include "dsa_sparse_mla.h"
 #include "fwd_kernel.hpp"
 #include "fwd_kernel_ws.hpp"
+#include "bwd_kernel.hpp"
 
 namespace {
 
@@ -270,6 +271,80 @@ int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stri
   st = device_check();
   if (st != DSA_OK) return st;
   return launch<true>(a, static_cast<hipStream_t>(stream));
+}
+
+int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_head, const void* kv,
+                       int64_t kv_stride_row, int64_t num_kv, const int32_t* indices,
+                       int64_t idx_stride_tok, int64_t num_tokens, int32_t num_heads, int32_t topk,
+                       float sm_scale, const void* out, int64_t out_stride_tok, int64_t out_stride_head,
+                       const float* lse, int64_t lse_stride_tok, const void* dout, int64_t dout_stride_tok,
+                       int64_t dout_stride_head, float* dq, int64_t dq_stride_tok, int64_t dq_stride_head,
+                       float* dkv, int64_t dkv_stride_row, void* stream) {
+  // q/out/lse checks are those of the forward (out and dout share its layout rules)
+  int st = check_common(q, q_stride_tok, q_stride_head, indices, idx_stride_tok, num_tokens, num_heads, topk,
+                        out, out_stride_tok, out_stride_head, lse, lse_stride_tok);
+  if (st != DSA_OK) return st;
+  if (!std::isfinite(sm_scale) || sm_scale < 0.f) return DSA_ERR_INVALID_ARGUMENT;
+  if (num_kv < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (num_kv > 0) {
+    if (!kv || !aligned(kv, 16) || kv_stride_row % 8 || kv_stride_row < (num_kv > 1 ? DSA_DQK : 0))
+      return DSA_ERR_INVALID_ARGUMENT;
+    if (!dkv || !aligned(dkv, 16) || dkv_stride_row % 4 || dkv_stride_row < DSA_DQK)
+      return DSA_ERR_INVALID_ARGUMENT;
+    if (num_kv > ((int64_t)1 << 32) - 1) return DSA_ERR_UNSUPPORTED;   // row ids are 32-bit
+  }
+  if (num_tokens > 0) {
+    if (!dout || !dq || !aligned(dout, 16) || !aligned(dq, 4)) return DSA_ERR_INVALID_ARGUMENT;
+    if (dout_stride_tok < 0 || dout_stride_head < 0 || dout_stride_tok % 8 || dout_stride_head % 8)
+      return DSA_ERR_INVALID_ARGUMENT;
+    if (dq_stride_tok < 0 || dq_stride_head < 0) return DSA_ERR_INVALID_ARGUMENT;
+    if (num_tokens > 1 && (dout_stride_tok == 0 || dq_stride_tok == 0)) return DSA_ERR_INVALID_ARGUMENT;
+    if (num_heads > 1 && (dout_stride_head < DSA_DV || dq_stride_head < DSA_DQK)) return DSA_ERR_INVALID_ARGUMENT;
+  }
+  st = device_check();
+  if (st != DSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (num_kv > 0) {
+    const int64_t n4 = num_kv * (DSA_DQK / 4);
+    hipLaunchKernelGGL(dsa::dkv_zero_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dkv, num_kv,
+                       dkv_stride_row);
+    if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
+  }
+  if (num_tokens == 0) return DSA_OK;
+  dsa::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_st = q_stride_tok;
+  a.q_sh = q_stride_head;
+  a.kv = static_cast<const uint16_t*>(kv);
+  a.kv_st = kv_stride_row;
+  a.num_kv = num_kv;
+  a.idx = indices;
+  a.idx_st = idx_stride_tok;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.topk = topk;
+  a.scale = sm_scale;
+  a.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  a.out = static_cast<const uint16_t*>(out);
+  a.o_st = out_stride_tok;
+  a.o_sh = out_stride_head;
+  a.lse = lse;
+  a.lse_st = lse_stride_tok;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.do_st = dout_stride_tok;
+  a.do_sh = dout_stride_head;
+  a.dq = dq;
+  a.dq_st = dq_stride_tok;
+  a.dq_sh = dq_stride_head;
+  a.dkv = dkv;
+  a.dkv_st = dkv_stride_row;
+  a.head_blocks = (num_heads + dsa::kBwHeads - 1) / dsa::kBwHeads;
+  const int64_t wgs = num_tokens * a.head_blocks;
+  if (wgs >= ((int64_t)1 << 31)) return DSA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
+  return DSA_OK;
 }
 
 const char* dsa_status_string(int status) {

@@ -1,6 +1,6 @@
 /*
- * dsa_sparse_mla.h -- C ABI of the DSA sparse MLA forward for AMD Instinct
- * MI355X (gfx950).
+ * dsa_sparse_mla.h -- C ABI of the DSA sparse MLA forward (and its backward)
+ * for AMD Instinct MI355X (gfx950).
  *
  * The operation: for each query token t and query head h, attention over only
  * the KV rows that the token's index row names. One latent KV row per key is
@@ -147,6 +147,49 @@ int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stri
                              float* lse, int64_t lse_stride_tok,
                              int32_t num_splits, void* workspace, int64_t workspace_bytes,
                              void* stream);
+
+/*
+ * Sparse MLA backward over a flat KV array: the gradients of the forward's
+ * output O with respect to q and kv, for an upstream gradient dout.
+ * Pages: xtuner PR 2083, Motivation (the forward's output and LSE feed the
+ * backward that the page keeps); the prime-rl pull request 4078 that adds a
+ * `cudnn_flashmla` DSA backend (a separate DSA backward kernel, timed per
+ * call). LSE is taken as an auxiliary output with no upstream gradient.
+ *
+ * With J the valid entries of token t's row, P the forward's softmax weights
+ * (recomputed from q, kv and lse), dP = dout . V^T, D = dout . out and
+ * dS = P (dP - D), per head:
+ *   dq[t]          = sm_scale * dS . K
+ *   dkv[J]        += sm_scale * dS^T . q[t]     (all 576 columns)
+ *   dkv[J, 0:512] += P^T . dout[t]               (the value columns)
+ * Rows that no valid entry names get 0. Duplicates count once per occurrence.
+ *
+ * q, kv, indices, num_tokens, num_heads, topk, sm_scale: as in dsa_sparse_mla_fwd
+ *          (any topk up to 65536; the call does not split rows).
+ * out      bf16 [num_tokens, num_heads, 512]: the forward output for these inputs.
+ * lse      fp32 [num_tokens, num_heads]: the forward LSE for these inputs.
+ * dout     bf16 [num_tokens, num_heads, 512], strides as for out.
+ * dq       fp32 [num_tokens, num_heads, 576] (written); element (t,h,d) at
+ *          dq + t*dq_stride_tok + h*dq_stride_head + d.
+ * dkv      fp32 [num_kv, 576] (written: zeroed, then accumulated with atomic
+ *          adds, so the order of additions into a row is not fixed and two
+ *          calls may differ in the last bits); row i at dkv + i*dkv_stride_row.
+ *          16-byte aligned, dkv_stride_row a multiple of 4 and >= 576.
+ * stream   hipStream_t to enqueue on.
+ *
+ * Limits: 1 <= num_heads <= 128, 1 <= topk <= 65536. dq and dkv must not
+ * overlap the inputs or each other.
+ */
+int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                       const void* kv, int64_t kv_stride_row, int64_t num_kv,
+                       const int32_t* indices, int64_t idx_stride_tok,
+                       int64_t num_tokens, int32_t num_heads, int32_t topk, float sm_scale,
+                       const void* out, int64_t out_stride_tok, int64_t out_stride_head,
+                       const float* lse, int64_t lse_stride_tok,
+                       const void* dout, int64_t dout_stride_tok, int64_t dout_stride_head,
+                       float* dq, int64_t dq_stride_tok, int64_t dq_stride_head,
+                       float* dkv, int64_t dkv_stride_row,
+                       void* stream);
 
 /* Human-readable name of a dsa_status value (a static string). */
 const char* dsa_status_string(int status);

@@ -128,6 +128,47 @@ def test_paged_host_validation(over, status):
     assert _paged(**over) == status
 
 
+def _bwd(**over):
+    args = dict(q=FAKE, q_st=8 * 576, q_sh=576, kv=FAKE, kv_st=576, num_kv=100, idx=FAKE,
+                idx_st=2048, T=8, H=8, topk=2048, sm=0.04, out=FAKE, o_st=8 * 512, o_sh=512,
+                lse=FAKE, lse_st=8, do=FAKE, do_st=8 * 512, do_sh=512, dq=FAKE, dq_st=8 * 576,
+                dq_sh=576, dkv=FAKE, dkv_st=576, stream=None)
+    args.update(over)
+    a = args
+    return dsa.lib().dsa_sparse_mla_bwd(
+        a["q"], a["q_st"], a["q_sh"], a["kv"], a["kv_st"], a["num_kv"], a["idx"], a["idx_st"],
+        a["T"], a["H"], a["topk"], a["sm"], a["out"], a["o_st"], a["o_sh"], a["lse"], a["lse_st"],
+        a["do"], a["do_st"], a["do_sh"], a["dq"], a["dq_st"], a["dq_sh"], a["dkv"], a["dkv_st"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"T": -1}, INVALID),
+    ({"H": 0}, UNSUPPORTED),
+    ({"H": 129}, UNSUPPORTED),
+    ({"topk": 65537}, UNSUPPORTED),
+    ({"q": None}, INVALID),
+    ({"out": None}, INVALID),
+    ({"lse": None}, INVALID),
+    ({"do": None}, INVALID),
+    ({"dq": None}, INVALID),
+    ({"dkv": None}, INVALID),
+    ({"kv": None}, INVALID),
+    ({"do": FAKE + 8}, INVALID),                      # dout not 16-byte aligned
+    ({"dkv": FAKE + 4}, INVALID),                     # dkv not 16-byte aligned
+    ({"dkv_st": 574}, INVALID),                       # not a multiple of 4
+    ({"dkv_st": 572}, INVALID),                       # rows overlap
+    ({"do_sh": 256}, INVALID),
+    ({"dq_sh": 512}, INVALID),                        # dq rows are 576 wide
+    ({"do_st": 0}, INVALID),
+    ({"sm": float("nan")}, INVALID),
+    ({"sm": -1.0}, INVALID),
+    ({"num_kv": -1}, INVALID),
+])
+def test_bwd_host_validation(over, status):
+    assert _bwd(**over) == status
+
+
 def test_valid_call_reaches_the_device_check():
     """A well-formed call passes validation; without a GPU the device check fails
     with a HIP status (and nothing is launched). On a GPU machine this test is not

@@ -1,0 +1,176 @@
+"""GPU parity of the HIP sparse MLA backward against the CPU backward oracle.
+
+Every case calls the backward through the C ABI and compares dq and dkv
+element by element with oracle/ (fp64, recomputed from q, kv, indices and
+dout alone). The parity cases hand the kernel the oracle's forward output
+(rounded to bf16, as a forward returns it) and LSE, so that only the
+backward's own arithmetic is measured; one end-to-end case feeds it the
+library's own forward instead, as a training step does.
+
+Tolerance. The pages fix none for the backward; this one follows from the
+arithmetic. The kernel rounds sm_scale*dS (and P) to bf16, unit roundoff
+2^-8, before its MFMA products; every other operand is an exact bf16 input
+and sums are fp32. A CPU emulation of exactly that rounding on the SWE-like
+workload gives a relative Frobenius error of 1.6e-3 for dq, and no element
+of dq beyond 0.014 * (|ref| + rms of the token's dq). The bound here is
+twice that, 3e-2 * (|ref| + rms of the token's row of the result: dq over
+its heads and columns, dkv over its 576 columns), plus the Frobenius bound
+1e-2. Both add an absolute 1e-4 per element: dS = P (dP - D) subtracts two
+fp32 dot products of 512 terms (magnitude ~20, rounding ~1e-6 each), and
+where they cancel exactly (one key: P = 1, D = dP) the reference is 0 while
+the kernel keeps that residue. End to end, D = dout . out also carries the
+forward's own rounding (its O is within the forward's 2e-2 tolerance), an
+error common to every key of a token; that case keeps the Frobenius bound
+and checks elements only against gross error (1e-1).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import sparse_mla_bwd_ref, sparse_mla_fwd_ref
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _dsa():
+    import dsa_sparse_mla_amd as dsa
+    return dsa
+
+
+def np64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def check_grad(x, ref, label, elem_tol=3e-2):
+    x = np.asarray(x, dtype=np.float64)
+    assert np.isfinite(x).all(), f"{label}: non-finite values"
+    # scale per first-axis row (one token's dq, one kv row's dkv): rows
+    # differ in magnitude (tokens with few keys have larger gradients)
+    rows = ref.reshape(ref.shape[0], -1)
+    rms_row = np.sqrt(np.mean(rows ** 2, axis=1, keepdims=True))
+    rms = float(np.sqrt(np.mean(rows ** 2)))
+    err = np.abs(x - ref).reshape(rows.shape)
+    bad = err > elem_tol * (np.abs(rows) + rms_row) + 1e-4
+    fro, rfro = np.linalg.norm(x - ref), np.linalg.norm(ref)
+    print(f"[{label}] max|d|={err.max():.3e} rms(ref)={rms:.3e} rel_fro={fro / max(rfro, 1e-30):.3e}")
+    assert not bad.any(), f"{label}: {bad.sum()} elements outside tolerance, max err {err.max()}"
+    assert fro <= 1e-2 * rfro + 1e-4 * np.sqrt(ref.size), f"{label}: Frobenius error {fro} of {rfro}"
+
+
+def run(q, kv, idx, sm, dout, own_forward=False):
+    """The backward on the GPU. out/lse: the oracle's forward (out rounded to
+    bf16), or with own_forward the library's forward on the same inputs."""
+    dsa = _dsa()
+    qd, kd, idd, dod = q.to(DEV), kv.to(DEV), idx.to(DEV), dout.to(DEV)
+    if own_forward:
+        out, lse = dsa.sparse_mla_fwd(qd, kd, idd, sm)
+    else:
+        o, l = sparse_mla_fwd_ref(np64(q), np64(kv), idx.cpu().numpy(), sm)
+        out = torch.from_numpy(o).to(torch.bfloat16).to(DEV)
+        lse = torch.from_numpy(l).float().to(DEV)
+    dq, dkv = dsa.sparse_mla_bwd(qd, kd, idd, sm, out, lse, dod)
+    torch.cuda.synchronize()
+    return dq, dkv
+
+
+def ref(q, kv, idx, sm, dout):
+    return sparse_mla_bwd_ref(np64(q), np64(kv), idx.cpu().numpy(), sm, np64(dout))
+
+
+def random_case(T, H, N, topk, seed, pad_frac=0.3, junk=True, dup=True):
+    g = torch.Generator().manual_seed(seed)
+    rng = np.random.default_rng(seed)
+    q = torch.randn((T, H, 576), generator=g).to(torch.bfloat16)
+    kv = torch.randn((N, 576), generator=g).to(torch.bfloat16)
+    dout = torch.randn((T, H, 512), generator=g).to(torch.bfloat16)
+    idx = rng.integers(0, N, size=(T, topk)).astype(np.int32)
+    if not dup:
+        idx = np.stack([rng.permutation(N)[:topk] for _ in range(T)]).astype(np.int32)
+    idx[rng.random((T, topk)) < pad_frac] = -1
+    if junk:
+        j = rng.random((T, topk)) < 0.05
+        idx[j] = rng.choice(np.array([N, N + 3, -7], dtype=np.int64), size=int(j.sum())).astype(np.int32)
+    return q, kv, torch.from_numpy(idx), dout
+
+
+@pytest.mark.parametrize("H", [1, 8, 16, 17, 64])
+def test_bwd_head_counts(H):
+    q, kv, idx, dout = random_case(48, H, 300, 100, seed=H)
+    dq, dkv = run(q, kv, idx, 1 / 24, dout)
+    rdq, rdkv = ref(q, kv, idx, 1 / 24, dout)
+    check_grad(np64(dq), rdq, f"dq H={H}")
+    check_grad(np64(dkv), rdkv, f"dkv H={H}")
+
+
+@pytest.mark.parametrize("topk", [1, 31, 33, 64, 2049, 4500])
+def test_bwd_topk_and_segments(topk):
+    """Ragged last tiles, a single key, and rows longer than one 2048-entry segment."""
+    q, kv, idx, dout = random_case(24, 8, 5000, topk, seed=100 + topk)
+    dq, dkv = run(q, kv, idx, 1 / 24, dout)
+    rdq, rdkv = ref(q, kv, idx, 1 / 24, dout)
+    check_grad(np64(dq), rdq, f"dq topk={topk}")
+    check_grad(np64(dkv), rdkv, f"dkv topk={topk}")
+
+
+def test_bwd_empty_rows_and_untouched_kv():
+    q, kv, idx, dout = random_case(16, 8, 400, 64, seed=7, dup=False)
+    idx[3] = -1                        # a token with no key
+    idx[9, :] = 450                    # only out-of-range values
+    dq, dkv = run(q, kv, idx, 1 / 24, dout)
+    dq, dkv = np64(dq), np64(dkv)
+    assert np.all(dq[3] == 0) and np.all(dq[9] == 0)
+    named = set(int(v) for v in idx.numpy().ravel() if 0 <= v < 400)
+    untouched = [r for r in range(400) if r not in named]
+    assert len(untouched) > 0 and np.all(dkv[untouched] == 0)
+    rdq, rdkv = ref(q, kv, idx, 1 / 24, dout)
+    check_grad(dq, rdq, "dq empty rows")
+    check_grad(dkv, rdkv, "dkv empty rows")
+
+
+def test_bwd_duplicates_add_up():
+    """A row named twice by one token gets twice that token's contribution."""
+    q, kv, idx, dout = random_case(8, 8, 200, 40, seed=11, pad_frac=0.0, junk=False, dup=False)
+    idx2 = idx.clone()
+    idx2[:, 20:] = idx[:, :20]         # the first 20 entries, twice each
+    dq, dkv = run(q, kv, idx2, 1 / 24, dout)
+    rdq, rdkv = ref(q, kv, idx2, 1 / 24, dout)
+    check_grad(np64(dq), rdq, "dq duplicates")
+    check_grad(np64(dkv), rdkv, "dkv duplicates")
+
+
+def test_bwd_swe_workload_full():
+    """The SWE-like prefill (2119 tokens, 8 heads, topk 2048, shuffled -1
+    padding) at full size, every token and every kv row checked."""
+    d = workloads.make_flat("swe")
+    g = torch.Generator().manual_seed(5)
+    dout = torch.randn((d["q"].shape[0], 8, 512), generator=g).to(torch.bfloat16)
+    dq, dkv = run(d["q"], d["kv"], d["indices"], d["sm_scale"], dout)
+    rdq, rdkv = ref(d["q"], d["kv"], d["indices"], d["sm_scale"], dout)
+    check_grad(np64(dq), rdq, "dq swe")
+    check_grad(np64(dkv), rdkv, "dkv swe")
+
+
+def test_bwd_after_own_forward_swe():
+    """End to end: the library's forward, then its backward, on the full
+    SWE-like prefill."""
+    d = workloads.make_flat("swe")
+    g = torch.Generator().manual_seed(9)
+    dout = torch.randn((d["q"].shape[0], 8, 512), generator=g).to(torch.bfloat16)
+    dq, dkv = run(d["q"], d["kv"], d["indices"], d["sm_scale"], dout, own_forward=True)
+    rdq, rdkv = ref(d["q"], d["kv"], d["indices"], d["sm_scale"], dout)
+    check_grad(np64(dq), rdq, "dq swe end to end", elem_tol=1e-1)
+    check_grad(np64(dkv), rdkv, "dkv swe end to end", elem_tol=1e-1)
+
+
+def test_bwd_wide_heads_small():
+    d = workloads.make_flat("wide", num_tokens=160, topk=2048)
+    g = torch.Generator().manual_seed(6)
+    dout = torch.randn((160, 64, 512), generator=g).to(torch.bfloat16)
+    dq, dkv = run(d["q"], d["kv"], d["indices"], d["sm_scale"], dout)
+    rdq, rdkv = ref(d["q"], d["kv"], d["indices"], d["sm_scale"], dout)
+    check_grad(np64(dq), rdq, "dq wide160")
+    check_grad(np64(dkv), rdkv, "dkv wide160")
