@@ -8,6 +8,12 @@ Default workload: SWE-like prefill, sq = skv = 2119 tokens, 8 query heads,
 dqk 576 / dv 512, topk 2048, bf16 (the shape of "feat: add XTuner TileLang
 sparse MLA backend", Performance > Isolated sparse MLA forward).
 
+With --op bwd it times the backward instead (flat workloads): one step is
+the dkv zero fill and the backward kernel, after one forward that supplies
+out and LSE; `value` then counts 3456 bytes per valid key (the 1152-byte
+gathered row and its 2304-byte fp32 dkv addition) and `tflops` 5504 flops
+per valid key and head.
+
 Prints one JSON line. `value` is the gathered-KV bandwidth (1152 bytes per
 valid key: one 576-wide bf16 row, shared by every head) over the average step
 time; `tflops` counts 2 * H * (576 + 512) flops per valid key. `roofline`
@@ -33,6 +39,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "sparse MLA fwd TFLOP/s + gathered-KV GB/s (% roofline), topk=2048, dqk576/dv512"
 ROW_BYTES = 576 * 2
 FLOP_PER_KEY_HEAD = 2 * (576 + 512)
+# backward: QK^T (576), dO V^T (512), dQ (576), dK (576), dV (512) per key and head
+BWD_METRIC = "sparse MLA bwd TFLOP/s + gathered-KV/dKV GB/s (% roofline), topk=2048, dqk576/dv512"
+BWD_FLOP_PER_KEY_HEAD = 2 * (3 * 576 + 2 * 512)
+BWD_BYTES_PER_KEY = ROW_BYTES + 576 * 4   # the gathered row, and its fp32 dkv addition
 
 
 def source_hash() -> str:
@@ -182,6 +192,39 @@ def cpu_baseline(d, budget_s: float):
     }
 
 
+def cpu_baseline_bwd(d, dout, budget_s: float):
+    """Time the CPU backward oracle on the last tokens of the workload until ~budget_s."""
+    from oracle import sparse_mla_bwd_ref
+    q = d["q"].float().cpu().numpy()
+    kv = d["kv"].float().cpu().numpy()
+    idx = d["indices"].cpu().numpy()
+    do = dout.float().cpu().numpy()
+    T = q.shape[0]
+    done_keys = done_tokens = 0
+    elapsed = 0.0
+    t_end = T
+    while elapsed < budget_s and t_end > 0:
+        a, b = max(0, t_end - 16), t_end
+        t0 = time.perf_counter()
+        sparse_mla_bwd_ref(q[a:b], kv, idx[a:b], d["sm_scale"], do[a:b])
+        elapsed += time.perf_counter() - t0
+        done_keys += int(((idx[a:b] >= 0) & (idx[a:b] < kv.shape[0])).sum())
+        done_tokens += b - a
+        t_end = a
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {
+        "value": round(done_keys * BWD_BYTES_PER_KEY / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"last {done_tokens} of {T} tokens ({done_keys} valid keys), backward oracle, "
+                  f"numpy float64, {elapsed:.1f} s",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +232,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="swe",
                     choices=["short", "swe", "wide", "varlen16k", "varlen32k", "decode"])
+    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd"],
+                    help="fwd (the headline metric) or the backward (flat workloads)")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 skips it)")
@@ -237,7 +282,20 @@ def main():
     splits, ws_bytes = dsa.workspace_size(T, H, d["indices"].shape[1], args.num_splits)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
-    if "kv" in d:
+    if args.op == "bwd":
+        if "kv" not in d:
+            print("the backward runs on flat workloads only", file=sys.stderr)
+            sys.exit(2)
+        g = torch.Generator(device=dev).manual_seed(12345)
+        dout = torch.randn((T, H, 512), generator=g, device=dev).to(torch.bfloat16)
+        dsa.sparse_mla_fwd(d["q"], d["kv"], d["indices"], d["sm_scale"], out=out, lse=lse, workspace=ws)
+        dq = torch.empty((T, H, 576), dtype=torch.float32, device=dev)
+        dkv = torch.empty((d["kv"].shape[0], 576), dtype=torch.float32, device=dev)
+
+        def step():
+            dsa.sparse_mla_bwd(d["q"], d["kv"], d["indices"], d["sm_scale"], out, lse, dout,
+                               dq=dq, dkv=dkv)
+    elif "kv" in d:
         def step():
             dsa.sparse_mla_fwd(d["q"], d["kv"], d["indices"], d["sm_scale"], out=out, lse=lse,
                                num_splits=args.num_splits, workspace=ws)
@@ -288,6 +346,9 @@ def main():
         flushed_ms = fl[len(fl) // 2]
         del scratch
 
+    if args.op == "bwd":
+        gathered = V * BWD_BYTES_PER_KEY
+        flops = V * H * BWD_FLOP_PER_KEY_HEAD
     gbps = gathered / (ms_per_step * 1e-3) / 1e9
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     kern_gbps = gathered / (avg_ms * 1e-3) / 1e9
@@ -302,8 +363,10 @@ def main():
                 "unit": "TFLOP/s", "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic_for(args.workload)}
 
+    if args.op == "bwd" and roof["traffic"] is not None:
+        roof["traffic"] = None   # the stored counters are the forward's
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if args.op == "fwd" else BWD_METRIC,
         "value": round(gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -330,8 +393,14 @@ def main():
            if flushed_ms is not None else {}),
         "source_hash": source_hash(),
     }
+    if args.op == "bwd":
+        rec["config"]["op"] = "bwd"
+        rec["bytes_per_key"] = BWD_BYTES_PER_KEY
     if args.cpu_budget > 0:
-        rec["cpu_baseline"] = cpu_baseline(d_host if gen_dev == "cpu" else d, args.cpu_budget)
+        if args.op == "bwd":
+            rec["cpu_baseline"] = cpu_baseline_bwd(d_host if gen_dev == "cpu" else d, dout, args.cpu_budget)
+        else:
+            rec["cpu_baseline"] = cpu_baseline(d_host if gen_dev == "cpu" else d, args.cpu_budget)
     print(json.dumps(rec), flush=True)
 
 
