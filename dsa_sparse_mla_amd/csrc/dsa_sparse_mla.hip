@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 
 #include "dsa_sparse_mla.h"
@@ -99,6 +100,41 @@ int check_common(const void* q, int64_t q_st, int64_t q_sh, const int32_t* idx, 
   if (q_st % 8 || q_sh % 8 || o_st % 8 || o_sh % 8) return DSA_ERR_INVALID_ARGUMENT;
   if (T > 1 && (q_st == 0 || o_st == 0 || idx_st < topk || lse_st < H)) return DSA_ERR_INVALID_ARGUMENT;
   if (H > 1 && (q_sh < DSA_DQK || o_sh < DSA_DV)) return DSA_ERR_INVALID_ARGUMENT;
+  return DSA_OK;
+}
+
+// Byte ranges [lo, hi) of strided tensors, for the check that no output
+// overlaps an input or another output. An empty tensor has lo == hi.
+struct Extent {
+  uintptr_t lo = 0, hi = 0;
+};
+// rows x cols elements of `bytes` each, rows `stride` elements apart
+Extent extent2(const void* p, int64_t rows, int64_t stride, int64_t cols, int64_t bytes) {
+  Extent e;
+  if (!p || rows <= 0 || cols <= 0) return e;
+  e.lo = reinterpret_cast<uintptr_t>(p);
+  e.hi = e.lo + (uintptr_t)(((rows - 1) * stride + cols) * bytes);
+  return e;
+}
+// [d0, d1, cols] with strides (s0, s1, 1)
+Extent extent3(const void* p, int64_t d0, int64_t s0, int64_t d1, int64_t s1, int64_t cols, int64_t bytes) {
+  Extent e;
+  if (!p || d0 <= 0 || d1 <= 0 || cols <= 0) return e;
+  e.lo = reinterpret_cast<uintptr_t>(p);
+  e.hi = e.lo + (uintptr_t)(((d0 - 1) * s0 + (d1 - 1) * s1 + cols) * bytes);
+  return e;
+}
+bool overlap(const Extent& a, const Extent& b) {
+  return a.hi > a.lo && b.hi > b.lo && a.lo < b.hi && b.lo < a.hi;
+}
+// DSA_ERR_INVALID_ARGUMENT if an output overlaps an input or another output
+int check_overlaps(std::initializer_list<Extent> outs, std::initializer_list<Extent> ins) {
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
+    for (const Extent& i : ins)
+      if (overlap(*o, i)) return DSA_ERR_INVALID_ARGUMENT;
+    for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+      if (overlap(*o, *o2)) return DSA_ERR_INVALID_ARGUMENT;
+  }
   return DSA_OK;
 }
 
@@ -214,6 +250,17 @@ int dsa_sparse_mla_fwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
   a.kv = static_cast<const uint8_t*>(kv);
   a.kv_row_gran = kv_stride_row / 8;
   a.num_kv = num_kv;
+  {
+    int64_t ws_need = 0;
+    int sp = 0, sl = 0;
+    check_splits(num_tokens, num_heads, topk, num_splits, &sp, &sl, &ws_need);
+    st = check_overlaps(
+        {extent3(out, num_tokens, out_stride_tok, num_heads, out_stride_head, DSA_DV, 2),
+         extent2(lse, num_tokens, lse_stride_tok, num_heads, 4), extent2(ws_need > 0 ? workspace : nullptr, 1, 0, ws_need, 1)},
+        {extent3(q, num_tokens, q_stride_tok, num_heads, q_stride_head, DSA_DQK, 2),
+         extent2(kv, num_kv, kv_stride_row, DSA_DQK, 2), extent2(indices, num_tokens, idx_stride_tok, topk, 4)});
+    if (st != DSA_OK) return st;
+  }
   st = device_check();
   if (st != DSA_OK) return st;
   return launch<false>(a, static_cast<hipStream_t>(stream));
@@ -268,6 +315,20 @@ int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stri
   a.seq_lens = seq_lens;
   a.q_per_seq = q_per_seq;
   a.num_pages = num_pages;
+  {
+    int64_t ws_need = 0;
+    int sp = 0, sl = 0;
+    check_splits(T, num_heads, topk, num_splits, &sp, &sl, &ws_need);
+    st = check_overlaps(
+        {extent3(out, T, out_stride_tok, num_heads, out_stride_head, DSA_DV, 2),
+         extent2(lse, T, lse_stride_tok, num_heads, 4), extent2(ws_need > 0 ? workspace : nullptr, 1, 0, ws_need, 1)},
+        {extent3(q, T, q_stride_tok, num_heads, q_stride_head, DSA_DQK, 2),
+         extent3(kv_pages, num_pages, kv_stride_page, page_size, kv_stride_row, DSA_DQK, 2),
+         extent2(indices, T, idx_stride_tok, topk, 4),
+         extent2(page_table, num_seqs, page_table_stride, max_pages_per_seq, 4),
+         extent2(seq_lens, 1, 0, num_seqs, 4)});
+    if (st != DSA_OK) return st;
+  }
   st = device_check();
   if (st != DSA_OK) return st;
   return launch<true>(a, static_cast<hipStream_t>(stream));
@@ -301,6 +362,15 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
     if (num_tokens > 1 && (dout_stride_tok == 0 || dq_stride_tok == 0)) return DSA_ERR_INVALID_ARGUMENT;
     if (num_heads > 1 && (dout_stride_head < DSA_DV || dq_stride_head < DSA_DQK)) return DSA_ERR_INVALID_ARGUMENT;
   }
+  st = check_overlaps(
+      {extent3(dq, num_tokens, dq_stride_tok, num_heads, dq_stride_head, DSA_DQK, 4),
+       extent2(dkv, num_kv, dkv_stride_row, DSA_DQK, 4)},
+      {extent3(q, num_tokens, q_stride_tok, num_heads, q_stride_head, DSA_DQK, 2),
+       extent2(kv, num_kv, kv_stride_row, DSA_DQK, 2), extent2(indices, num_tokens, idx_stride_tok, topk, 4),
+       extent3(out, num_tokens, out_stride_tok, num_heads, out_stride_head, DSA_DV, 2),
+       extent2(lse, num_tokens, lse_stride_tok, num_heads, 4),
+       extent3(dout, num_tokens, dout_stride_tok, num_heads, dout_stride_head, DSA_DV, 2)});
+  if (st != DSA_OK) return st;
   st = device_check();
   if (st != DSA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);

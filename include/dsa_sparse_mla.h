@@ -43,6 +43,10 @@
  *     kernel through the caller's workspace. Shorter rows may also be split
  *     for parallelism (num_splits = 0 lets the library choose).
  *   - Every entry point returns a dsa_status and never throws.
+ *   - Outputs may not overlap inputs or other outputs. The host compares byte
+ *     extents (first to last element of each strided tensor), so two views
+ *     that interleave inside one allocation are rejected even where they
+ *     share no element.
  */
 #ifndef DSA_SPARSE_MLA_H
 #define DSA_SPARSE_MLA_H
@@ -104,7 +108,8 @@ int dsa_sparse_mla_workspace_size(int64_t num_tokens, int32_t num_heads, int32_t
  * stream   hipStream_t to enqueue on.
  *
  * Limits: 1 <= num_heads <= 128, 1 <= topk <= 65536, num_kv * kv_stride_row * 2
- * bytes < 64 GiB. out and lse must not overlap the inputs.
+ * bytes < 64 GiB. out, lse and the workspace must not overlap the inputs or
+ * each other (checked on the host: DSA_ERR_INVALID_ARGUMENT).
  */
 int dsa_sparse_mla_fwd(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
                        const void* kv, int64_t kv_stride_row, int64_t num_kv,
@@ -178,7 +183,7 @@ int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stri
  * stream   hipStream_t to enqueue on.
  *
  * Limits: 1 <= num_heads <= 128, 1 <= topk <= 65536. dq and dkv must not
- * overlap the inputs or each other.
+ * overlap the inputs or each other (checked on the host: DSA_ERR_INVALID_ARGUMENT).
  */
 int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
                        const void* kv, int64_t kv_stride_row, int64_t num_kv,

@@ -19,6 +19,11 @@ OK, INVALID, UNSUPPORTED, HIPERR, WORKSPACE = 0, 1, 2, 3, 4
 FAKE = 0x10000  # a 64 KiB-aligned non-null address; never dereferenced by the host checks
 
 
+def fake(i: int) -> int:
+    """Distinct fake buffers, 1 TiB apart, so that only the overlap cases overlap."""
+    return FAKE + (i << 40)
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -49,9 +54,9 @@ def test_version_and_status_strings():
 
 
 def _fwd(**over):
-    args = dict(q=FAKE, q_st=8 * 576, q_sh=576, kv=FAKE, kv_st=576, num_kv=100, idx=FAKE,
-                idx_st=2048, T=8, H=8, topk=2048, sm=0.04, out=FAKE, o_st=8 * 512, o_sh=512,
-                lse=FAKE, lse_st=8, splits=1, ws=None, ws_bytes=0, stream=None)
+    args = dict(q=fake(0), q_st=8 * 576, q_sh=576, kv=fake(1), kv_st=576, num_kv=100, idx=fake(2),
+                idx_st=2048, T=8, H=8, topk=2048, sm=0.04, out=fake(3), o_st=8 * 512, o_sh=512,
+                lse=fake(4), lse_st=8, splits=1, ws=None, ws_bytes=0, stream=None)
     args.update(over)
     return dsa.lib().dsa_sparse_mla_fwd(
         args["q"], args["q_st"], args["q_sh"], args["kv"], args["kv_st"], args["num_kv"],
@@ -72,9 +77,15 @@ def _fwd(**over):
     ({"idx": None}, INVALID),
     ({"out": None}, INVALID),
     ({"lse": None}, INVALID),
-    ({"q": FAKE + 8}, INVALID),                       # q not 16-byte aligned
-    ({"kv": FAKE + 2}, INVALID),
-    ({"lse": FAKE + 2}, INVALID),
+    ({"q": fake(0) + 8}, INVALID),                    # q not 16-byte aligned
+    ({"kv": fake(1) + 2}, INVALID),
+    ({"lse": fake(4) + 2}, INVALID),
+    ({"out": fake(0)}, INVALID),                      # out overlaps q
+    ({"out": fake(0) + 2 * 8 * 8 * 576 - 16}, INVALID),  # ... by its last 16 bytes
+    ({"lse": fake(2) + 4 * 8 * 2048 - 4}, INVALID),   # lse overlaps the last index
+    ({"lse": fake(3) + 100}, INVALID),                # lse inside out
+    ({"kv": fake(3)}, INVALID),                       # out overlaps kv
+    ({"splits": 4, "ws": fake(0), "ws_bytes": 8 * 4 * 8 * 514 * 4}, INVALID),   # workspace over q
     ({"q_sh": 577}, INVALID),                         # stride not a multiple of 8
     ({"kv_st": 572}, INVALID),
     ({"kv_st": 100}, INVALID),                        # rows overlap
@@ -88,7 +99,7 @@ def _fwd(**over):
     ({"splits": 3000}, INVALID),                      # more splits than entries
     ({"topk": 5000, "splits": 2}, INVALID),           # fewer than ceil(5000 / 2048)
     ({"splits": 4}, WORKSPACE),                       # a split needs workspace
-    ({"splits": 4, "ws": FAKE, "ws_bytes": 100}, WORKSPACE),
+    ({"splits": 4, "ws": fake(5), "ws_bytes": 100}, WORKSPACE),
     ({"num_kv": 1 << 40}, UNSUPPORTED),               # offsets past 64 GiB
 ])
 def test_fwd_host_validation(over, status):
@@ -96,9 +107,9 @@ def test_fwd_host_validation(over, status):
 
 
 def _paged(**over):
-    args = dict(q=FAKE, q_st=8 * 576, q_sh=576, kvp=FAKE, pst=64 * 576, rst=576, P=10, ps=64,
-                pt=FAKE, pt_st=16, maxp=16, sl=FAKE, idx=FAKE, idx_st=2048, S=4, Q=2, H=8,
-                topk=2048, sm=0.04, out=FAKE, o_st=8 * 512, o_sh=512, lse=FAKE, lse_st=8,
+    args = dict(q=fake(0), q_st=8 * 576, q_sh=576, kvp=fake(1), pst=64 * 576, rst=576, P=10, ps=64,
+                pt=fake(6), pt_st=16, maxp=16, sl=fake(7), idx=fake(2), idx_st=2048, S=4, Q=2, H=8,
+                topk=2048, sm=0.04, out=fake(3), o_st=8 * 512, o_sh=512, lse=fake(4), lse_st=8,
                 splits=1, ws=None, ws_bytes=0, stream=None)
     args.update(over)
     a = args
@@ -123,16 +134,19 @@ def _paged(**over):
     ({"rst": 576 + 4}, INVALID),
     ({"H": 200}, UNSUPPORTED),
     ({"P": 1 << 40}, UNSUPPORTED),
+    ({"lse": fake(6)}, INVALID),                      # lse over the page table
+    ({"out": fake(7)}, INVALID),                      # out over seq_lens
+    ({"out": fake(1) + 64 * 576 * 2 * 9}, INVALID),   # out inside the last page
 ])
 def test_paged_host_validation(over, status):
     assert _paged(**over) == status
 
 
 def _bwd(**over):
-    args = dict(q=FAKE, q_st=8 * 576, q_sh=576, kv=FAKE, kv_st=576, num_kv=100, idx=FAKE,
-                idx_st=2048, T=8, H=8, topk=2048, sm=0.04, out=FAKE, o_st=8 * 512, o_sh=512,
-                lse=FAKE, lse_st=8, do=FAKE, do_st=8 * 512, do_sh=512, dq=FAKE, dq_st=8 * 576,
-                dq_sh=576, dkv=FAKE, dkv_st=576, stream=None)
+    args = dict(q=fake(0), q_st=8 * 576, q_sh=576, kv=fake(1), kv_st=576, num_kv=100, idx=fake(2),
+                idx_st=2048, T=8, H=8, topk=2048, sm=0.04, out=fake(3), o_st=8 * 512, o_sh=512,
+                lse=fake(4), lse_st=8, do=fake(5), do_st=8 * 512, do_sh=512, dq=fake(6), dq_st=8 * 576,
+                dq_sh=576, dkv=fake(7), dkv_st=576, stream=None)
     args.update(over)
     a = args
     return dsa.lib().dsa_sparse_mla_bwd(
@@ -154,8 +168,12 @@ def _bwd(**over):
     ({"dq": None}, INVALID),
     ({"dkv": None}, INVALID),
     ({"kv": None}, INVALID),
-    ({"do": FAKE + 8}, INVALID),                      # dout not 16-byte aligned
-    ({"dkv": FAKE + 4}, INVALID),                     # dkv not 16-byte aligned
+    ({"do": fake(5) + 8}, INVALID),                   # dout not 16-byte aligned
+    ({"dkv": fake(7) + 4}, INVALID),                  # dkv not 16-byte aligned
+    ({"dq": fake(5)}, INVALID),                       # dq over dout
+    ({"dkv": fake(6)}, INVALID),                      # dkv over dq
+    ({"dkv": fake(1)}, INVALID),                      # dkv over kv
+    ({"dq": fake(0) + 16}, INVALID),                  # dq inside q
     ({"dkv_st": 574}, INVALID),                       # not a multiple of 4
     ({"dkv_st": 572}, INVALID),                       # rows overlap
     ({"do_sh": 256}, INVALID),
@@ -177,6 +195,9 @@ def test_valid_call_reaches_the_device_check():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _fwd() in (HIPERR, UNSUPPORTED)
+    # out right after q (adjacent, not overlapping) passes the overlap check too
+    assert _fwd(out=fake(0) + 2 * 8 * 8 * 576) in (HIPERR, UNSUPPORTED)
+    assert _bwd() in (HIPERR, UNSUPPORTED)
 
 
 @pytest.mark.parametrize("T,H,topk,req,splits,nbytes", [
