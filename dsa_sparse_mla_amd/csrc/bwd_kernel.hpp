@@ -11,7 +11,8 @@
 //   dkv[J,:512] += P^T dO             (the value use)
 // Entries that name no row get nothing; duplicates count once per occurrence.
 //
-// One workgroup of 4 waves handles one token and a block of 16 heads. The
+// One workgroup of 4 waves handles one token and a block of 16 heads (32 when
+// the call has more than 16 heads: see the kernel's HT). The
 // index row is compacted per 2048-entry segment, as in the forward. Per tile
 // of 32 keys:
 //   phase 1: waves 0,1: S^T = K Q^T on key block 0 / 1 (16x16x32 MFMA, Q^T
@@ -62,7 +63,6 @@ struct BwdArgs {
   int32_t head_blocks;     // workgroups per token (16 heads each)
 };
 
-constexpr int kBwHeads = 16;
 constexpr int kBwPitch = 1168;                  // LDS row pitch of K rows and Q rows: 1152 + 16
 constexpr int kBwStage = kTileKeys * kBwPitch;  // one tile of 32 rows
 constexpr int kBwOPitch = 1040;                 // LDS row pitch of dO rows: 1024 + 16
@@ -70,43 +70,51 @@ constexpr int kBwGran = kTileKeys * (kDqk / 8) / 256;   // 16-byte granules per 
 static_assert(kTileKeys * (kDqk / 8) % 256 == 0, "a tile splits evenly over the threads");
 
 __device__ __forceinline__ bf16x8_t lds16(const uint8_t* p) { return *(const bf16x8_t*)p; }
+__device__ __forceinline__ bf16x8_t join4(short4_t lo, short4_t hi) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
+// HT head tiles of 16 per workgroup (1 or 2). With 2, each key's dkv row is
+// added once per 32 heads instead of once per 16, and each tile is gathered
+// once for 32 heads.
+template <int HT>
 __global__ void __launch_bounds__(256)
 sparse_mla_bwd_kernel(const BwdArgs a) {
+  constexpr int HB = 16 * HT;   // heads of the workgroup
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[2][kBwStage];
-  __shared__ __attribute__((aligned(16))) uint8_t s_q[kBwHeads * kBwPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t s_do[kBwHeads * kBwOPitch];
-  __shared__ __attribute__((aligned(16))) float4_t s_dp[2][64];          // dP^T of key block 0 / 1
-  __shared__ __attribute__((aligned(16))) uint8_t s_pt[kBwHeads * 64];   // P, bf16 [head][32 keys]
-  __shared__ __attribute__((aligned(16))) uint8_t s_dst[kBwHeads * 64];  // s*dS, bf16 [head][32 keys]
-  __shared__ __attribute__((aligned(16))) uint32_t s_rows[kSegment];     // compacted row ids
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[HB * kBwPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t s_do[HB * kBwOPitch];
+  __shared__ __attribute__((aligned(16))) float4_t s_dp[2][HT][64];   // dP^T of key block 0 / 1, head tile
+  __shared__ __attribute__((aligned(16))) uint8_t s_pt[HB * 64];      // P, bf16 [head][32 keys]
+  __shared__ __attribute__((aligned(16))) uint8_t s_dst[HB * 64];     // s*dS, bf16 [head][32 keys]
+  __shared__ __attribute__((aligned(16))) uint32_t s_rows[kSegment];  // compacted row ids
   __shared__ int s_cnt[kChunks];
-  __shared__ float s_D[kBwHeads], s_lse2[kBwHeads];
+  __shared__ float s_D[HB], s_lse2[HB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;   // MFMA column / k-group of the lane
   const int64_t token = blockIdx.x / a.head_blocks;
-  const int h0 = (int)(blockIdx.x % a.head_blocks) * kBwHeads;
+  const int h0 = (int)(blockIdx.x % a.head_blocks) * HB;
 
   // ---------------------------------------------------------------- per-token inputs
-  // Q (16 x 576) and dO (16 x 512) of the head block into LDS; padded heads are 0.
-  for (int i = tid; i < kBwHeads * (kDqk / 8); i += 256) {
+  // Q (HB x 576) and dO (HB x 512) of the head block into LDS; padded heads are 0.
+  for (int i = tid; i < HB * (kDqk / 8); i += 256) {
     const int h = i / (kDqk / 8), c = i % (kDqk / 8);
     bf16x8_t v = {};
     if (h0 + h < a.num_heads) v = *(const bf16x8_t*)(a.q + token * a.q_st + (int64_t)(h0 + h) * a.q_sh + 8 * c);
     *(bf16x8_t*)(s_q + h * kBwPitch + 16 * c) = v;
   }
-  for (int i = tid; i < kBwHeads * (kDv / 8); i += 256) {
+  for (int i = tid; i < HB * (kDv / 8); i += 256) {
     const int h = i / (kDv / 8), c = i % (kDv / 8);
     bf16x8_t v = {};
     if (h0 + h < a.num_heads) v = *(const bf16x8_t*)(a.dout + token * a.do_st + (int64_t)(h0 + h) * a.do_sh + 8 * c);
     *(bf16x8_t*)(s_do + h * kBwOPitch + 16 * c) = v;
   }
-  // D = dO . O and LSE (log2 units) per head: wave w takes heads 4w .. 4w+3
-  for (int hh = 0; hh < 4; ++hh) {
-    const int h = 4 * wave + hh;
+  // D = dO . O and LSE (log2 units) per head: wave w takes heads HB/4 * w ..
+  for (int hh = 0; hh < HB / 4; ++hh) {
+    const int h = (HB / 4) * wave + hh;
     float d = 0.f;
     if (h0 + h < a.num_heads) {
       const bf16x8_t o = *(const bf16x8_t*)(a.out + token * a.o_st + (int64_t)(h0 + h) * a.o_sh + 8 * lane);
@@ -124,19 +132,25 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
   }
   __syncthreads();
 
-  // Q^T (waves 0, 1) or dO^T (waves 2, 3) as the MFMA B operand: lane holds
-  // head n, columns 32c + 8g .. +7
+  // Q^T (waves 0, 1) or dO^T (waves 2, 3) as the MFMA B operand, head tile ht:
+  // lane holds head 16ht + n, columns 32c + 8g .. +7
   const bool s_role = wave < 2;
   const int kb = wave & 1;   // key block of the phase-1 product
-  bf16x8_t breg[kDqk / 32];
+  bf16x8_t breg[HT][kDqk / 32];
 #pragma unroll
-  for (int c = 0; c < kDqk / 32; ++c)
-    breg[c] = s_role ? lds16(s_q + n * kBwPitch + 2 * (32 * c + 8 * g))
-                     : (c < kDv / 32 ? lds16(s_do + n * kBwOPitch + 2 * (32 * c + 8 * g)) : (bf16x8_t){});
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int c = 0; c < kDqk / 32; ++c)
+      breg[ht][c] = s_role ? lds16(s_q + (16 * ht + n) * kBwPitch + 2 * (32 * c + 8 * g))
+                           : (c < kDv / 32 ? lds16(s_do + (16 * ht + n) * kBwOPitch + 2 * (32 * c + 8 * g))
+                                           : (bf16x8_t){});
 
-  float4_t dq_acc[9];   // dq tiles 9w .. 9w+8: lane holds column 16dt + n of heads 4g .. 4g+3
+  // dq tiles 9w .. 9w+8 of head tile ht: lane holds column 16dt + n of heads 16ht + 4g .. +3
+  float4_t dq_acc[HT][9];
 #pragma unroll
-  for (int k = 0; k < 9; ++k) dq_acc[k] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int k = 0; k < 9; ++k) dq_acc[ht][k] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
   FwdArgs fa = {};   // the forward's index stage, with row ids as the offsets
   fa.idx = a.idx;
@@ -179,67 +193,75 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
       if (j + 1 < ntiles) load_tile(j + 1);   // in flight during the three phases
       const uint8_t* st = s_stage[j & 1];
 
-      // ---- phase 1: S^T (waves 0, 1) or dP^T (waves 2, 3) of key block kb
-      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+      // ---- phase 1: S^T (waves 0, 1) or dP^T (waves 2, 3) of key block kb, every head tile
+      float4_t acc[HT];
       const uint8_t* arow = st + (kb * 16 + n) * kBwPitch + 16 * g;   // key kb*16 + n, columns 8g ..
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = (float4_t){0.f, 0.f, 0.f, 0.f};
       if (s_role) {
 #pragma unroll
-        for (int c = 0; c < kDqk / 32; ++c)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow + 64 * c), breg[c], acc, 0, 0, 0);
+        for (int c = 0; c < kDqk / 32; ++c) {
+          const bf16x8_t av = lds16(arow + 64 * c);
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht)
+            acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, breg[ht][c], acc[ht], 0, 0, 0);
+        }
       } else {
 #pragma unroll
-        for (int c = 0; c < kDv / 32; ++c)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow + 64 * c), breg[c], acc, 0, 0, 0);
-        s_dp[kb][lane] = acc;
+        for (int c = 0; c < kDv / 32; ++c) {
+          const bf16x8_t av = lds16(arow + 64 * c);
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht)
+            acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, breg[ht][c], acc[ht], 0, 0, 0);
+        }
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) s_dp[kb][ht][lane] = acc[ht];
       }
       __syncthreads();
 
-      // ---- phase 2: P and s*dS (lane: head n, keys kb*16 + 4g + e)
+      // ---- phase 2: P and s*dS (lane: head 16ht + n, keys kb*16 + 4g + e)
       if (s_role) {
-        const float4_t dp = s_dp[kb][lane];
-        const float Dh = s_D[n], l2 = s_lse2[n];
         const int lim = nvalid - j * kTileKeys;
-        float p[4], ds[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = kb * 16 + 4 * g + e < lim;
-          p[e] = ok ? __builtin_amdgcn_exp2f(acc[e] * a.scale_log2 - l2) : 0.f;
-          ds[e] = p[e] * (dp[e] - Dh) * a.scale;
+        for (int ht = 0; ht < HT; ++ht) {
+          const int h = 16 * ht + n;
+          const float4_t dp = s_dp[kb][ht][lane];
+          const float Dh = s_D[h], l2 = s_lse2[h];
+          float p[4], ds[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool ok = kb * 16 + 4 * g + e < lim;
+            p[e] = ok ? __builtin_amdgcn_exp2f(acc[ht][e] * a.scale_log2 - l2) : 0.f;
+            ds[e] = p[e] * (dp[e] - Dh) * a.scale;
+          }
+          const int off = h * 64 + 2 * (kb * 16 + 4 * g);
+          *(uint2*)(s_pt + off) = (uint2){pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+          *(uint2*)(s_dst + off) = (uint2){pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
         }
-        const int off = n * 64 + 2 * (kb * 16 + 4 * g);
-        *(uint2*)(s_pt + off) = (uint2){pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-        *(uint2*)(s_dst + off) = (uint2){pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
       }
       __syncthreads();
 
       // ---- phase 3a: dq tiles 9w .. 9w+8 += (s dS)[16 heads x 32 keys] K[32 keys x 16 columns]
       {
-        const bf16x8_t ads = lds16(s_dst + n * 64 + 16 * g);   // head n, keys 8g .. 8g+7
         // K^T operand: lane (g, n) points at key 8g + 4half + n/4, columns d0 + 4(n % 4)
         const uint8_t* kt = st + (8 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
+        bf16x8_t ads[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) ads[ht] = lds16(s_dst + (16 * ht + n) * 64 + 16 * g);   // keys 8g ..
 #pragma unroll
         for (int k = 0; k < 9; ++k) {
           const int d0 = 16 * (9 * wave + k);
-          const short4_t lo = lds_read_tr16(kt + 2 * d0);
-          const short4_t hi = lds_read_tr16(kt + 4 * kBwPitch + 2 * d0);
-          const bf16x8_t b = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          dq_acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads, b, dq_acc[k], 0, 0, 0);
+          const bf16x8_t b = join4(lds_read_tr16(kt + 2 * d0), lds_read_tr16(kt + 4 * kBwPitch + 2 * d0));
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht)
+            dq_acc[ht][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads[ht], b, dq_acc[ht][k], 0, 0, 0);
         }
       }
       // ---- phase 3b: dkv of key block kb2 = w >> 1, column tiles 18(w & 1) .. +17:
-      //   [16 keys x 16 columns] = (s dS)^T Q + P^T dO over the 16 heads
+      //   [16 keys x 16 columns] = (s dS)^T Q + P^T dO over the HB heads
       {
         const int kb2 = wave >> 1;
-        // A operands: lane (g, n) points at head 4g + n/4, keys kb2*16 + 4(n % 4);
-        // it receives key kb2*16 + n of heads 4g .. 4g+3
-        const int aoff = (4 * g + (n >> 2)) * 64 + 2 * (kb2 * 16 + 4 * (n & 3));
-        const short4_t ads = lds_read_tr16(s_dst + aoff);
-        const short4_t ap = lds_read_tr16(s_pt + aoff);
-        // B operands: lane (g, n) points at head 4g + n/4, columns d0 + 4(n % 4)
-        const uint8_t* bq = s_q + (4 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
-        const uint8_t* bo = s_do + (4 * g + (n >> 2)) * kBwOPitch + 8 * (n & 3);
-        // this lane's outputs: column d0 + n of keys kb2*16 + 4g + e
-        const int kbase = j * kTileKeys + kb2 * 16 + 4 * g;
+        const int kbase = j * kTileKeys + kb2 * 16 + 4 * g;   // this lane's outputs: keys kbase + e
         uint32_t rid[4];
         bool rok[4];
 #pragma unroll
@@ -247,15 +269,45 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
           rid[e] = s_rows[kbase + e];
           rok[e] = kbase + e < nvalid;
         }
+        if constexpr (HT == 1) {
+          // 16x16x16 over heads 4g .. 4g+3: A operands (lane (g, n) points at head
+          // 4g + n/4, keys kb2*16 + 4(n % 4)) receive key kb2*16 + n
+          const int aoff = (4 * g + (n >> 2)) * 64 + 2 * (kb2 * 16 + 4 * (n & 3));
+          const short4_t ads = lds_read_tr16(s_dst + aoff);
+          const short4_t ap = lds_read_tr16(s_pt + aoff);
+          const uint8_t* bq = s_q + (4 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
+          const uint8_t* bo = s_do + (4 * g + (n >> 2)) * kBwOPitch + 8 * (n & 3);
 #pragma unroll 2
-        for (int k = 0; k < 18; ++k) {
-          const int d0 = 16 * (18 * (wave & 1) + k);
-          float4_t c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ads, lds_read_tr16(bq + 2 * d0),
-                                                                 (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          if (d0 < kDv) c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap, lds_read_tr16(bo + 2 * d0), c, 0, 0, 0);
+          for (int k = 0; k < 18; ++k) {
+            const int d0 = 16 * (18 * (wave & 1) + k);
+            float4_t c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ads, lds_read_tr16(bq + 2 * d0),
+                                                                   (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            if (d0 < kDv) c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap, lds_read_tr16(bo + 2 * d0), c, 0, 0, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (rok[e]) unsafeAtomicAdd(a.dkv + (int64_t)rid[e] * a.dkv_st + d0 + n, c[e]);
+            for (int e = 0; e < 4; ++e)
+              if (rok[e]) unsafeAtomicAdd(a.dkv + (int64_t)rid[e] * a.dkv_st + d0 + n, c[e]);
+          }
+        } else {
+          // 16x16x32 over heads 8g .. 8g+7: two transposed reads per operand
+          // (heads 8g + n/4 and 8g + 4 + n/4)
+          const int aoff = (8 * g + (n >> 2)) * 64 + 2 * (kb2 * 16 + 4 * (n & 3));
+          const bf16x8_t ads = join4(lds_read_tr16(s_dst + aoff), lds_read_tr16(s_dst + aoff + 4 * 64));
+          const bf16x8_t ap = join4(lds_read_tr16(s_pt + aoff), lds_read_tr16(s_pt + aoff + 4 * 64));
+          const uint8_t* bq = s_q + (8 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
+          const uint8_t* bo = s_do + (8 * g + (n >> 2)) * kBwOPitch + 8 * (n & 3);
+#pragma unroll 2
+          for (int k = 0; k < 18; ++k) {
+            const int d0 = 16 * (18 * (wave & 1) + k);
+            const bf16x8_t b1 = join4(lds_read_tr16(bq + 2 * d0), lds_read_tr16(bq + 4 * kBwPitch + 2 * d0));
+            float4_t c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads, b1, (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            if (d0 < kDv) {
+              const bf16x8_t b2 = join4(lds_read_tr16(bo + 2 * d0), lds_read_tr16(bo + 4 * kBwOPitch + 2 * d0));
+              c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, b2, c, 0, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (rok[e]) unsafeAtomicAdd(a.dkv + (int64_t)rid[e] * a.dkv_st + d0 + n, c[e]);
+          }
         }
       }
       if (j + 1 < ntiles) store_tile(j + 1);   // the other stage: last read before this tile's barrier
@@ -265,14 +317,16 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
 
   // ---------------------------------------------------------------- dq (fp32)
 #pragma unroll
-  for (int k = 0; k < 9; ++k) {
-    const int d = 16 * (9 * wave + k) + n;
+  for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int h = h0 + 4 * g + e;
-      if (h < a.num_heads) a.dq[token * a.dq_st + (int64_t)h * a.dq_sh + d] = dq_acc[k][e];
+    for (int k = 0; k < 9; ++k) {
+      const int d = 16 * (9 * wave + k) + n;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int h = h0 + 16 * ht + 4 * g + e;
+        if (h < a.num_heads) a.dq[token * a.dq_st + (int64_t)h * a.dq_sh + d] = dq_acc[ht][k][e];
+      }
     }
-  }
 }
 
 // dkv = 0 before the backward accumulates into it: one thread per float4.

@@ -409,10 +409,16 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
   a.dq_sh = dq_stride_head;
   a.dkv = dkv;
   a.dkv_st = dkv_stride_row;
-  a.head_blocks = (num_heads + dsa::kBwHeads - 1) / dsa::kBwHeads;
+  // 16 heads per workgroup up to 16 heads, else 32 (each kv row's gradient is
+  // then added once per 32 heads)
+  const int hb = num_heads <= 16 ? 16 : 32;
+  a.head_blocks = (num_heads + hb - 1) / hb;
   const int64_t wgs = num_tokens * a.head_blocks;
   if (wgs >= ((int64_t)1 << 31)) return DSA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a);
+  if (hb == 16)
+    hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
   return DSA_OK;
 }

@@ -174,3 +174,33 @@ def test_bwd_wide_heads_small():
     rdq, rdkv = ref(d["q"], d["kv"], d["indices"], d["sm_scale"], dout)
     check_grad(np64(dq), rdq, "dq wide160")
     check_grad(np64(dkv), rdkv, "dkv wide160")
+
+
+def test_bwd_strided_and_many_heads():
+    """Strided q (every other head of a wider tensor), kv rows 640 apart, an
+    index row with trailing columns, dq/dkv views into larger buffers; and
+    128 heads (eight head blocks)."""
+    T, H, N, k = 20, 128, 500, 150
+    q_big, kv, idx, dout = random_case(T, 2 * H, N, k, seed=21)
+    dout = dout[:, :H].contiguous()
+    q = q_big[:, ::2]
+    kv_big = torch.zeros((N, 640), dtype=torch.bfloat16)
+    kv_big[:, :576] = kv
+    idx_big = torch.full((T, k + 8), -1, dtype=torch.int32)
+    idx_big[:, :k] = idx
+    dsa = _dsa()
+    qd = q_big.to(DEV)[:, ::2]
+    kvd = kv_big.to(DEV)[:, :576]
+    idd = idx_big.to(DEV)[:, :k]
+    o, l = sparse_mla_fwd_ref(np64(q), np64(kv), idx.numpy(), 1 / 24)
+    out = torch.from_numpy(o).to(torch.bfloat16).to(DEV)
+    lse = torch.from_numpy(l).float().to(DEV)
+    dq_big = torch.full((T, H, 640), 7.0, device=DEV)
+    dkv_big = torch.full((N, 600), 7.0, device=DEV)
+    dq, dkv = dsa.sparse_mla_bwd(qd, kvd, idd, 1 / 24, out, lse, dout.to(DEV),
+                                 dq=dq_big[:, :, :576], dkv=dkv_big[:, :576])
+    torch.cuda.synchronize()
+    assert (dq_big[:, :, 576:] == 7.0).all() and (dkv_big[:, 576:] == 7.0).all()
+    rdq, rdkv = ref(q, kv, idx, 1 / 24, dout)
+    check_grad(np64(dq), rdq, "dq strided H=128")
+    check_grad(np64(dkv), rdkv, "dkv strided H=128")
