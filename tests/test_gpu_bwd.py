@@ -97,7 +97,7 @@ def random_case(T, H, N, topk, seed, pad_frac=0.3, junk=True, dup=True):
     return q, kv, torch.from_numpy(idx), dout
 
 
-@pytest.mark.parametrize("H", [1, 8, 16, 17, 64])
+@pytest.mark.parametrize("H", [1, 8, 16, 17, 48, 64])
 def test_bwd_head_counts(H):
     q, kv, idx, dout = random_case(48, H, 300, 100, seed=H)
     dq, dkv = run(q, kv, idx, 1 / 24, dout)
