@@ -55,10 +55,15 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload: str):
-    """Measured HBM bytes per launch from the committed counter summary, if it
-    was taken on the current kernel sources; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def traffic_path(workload: str, op: str = "fwd") -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json" if op == "fwd"
+                        else f"traffic_bwd_{workload}.json")
+
+
+def traffic_for(workload: str, op: str = "fwd"):
+    """Measured HBM bytes per launch of the op's main kernel, from the committed
+    counter summary, if it was taken on the current kernel sources; otherwise None."""
+    path = traffic_path(workload, op)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -70,6 +75,7 @@ def traffic_for(workload: str):
 
 COPY_BYTES = 256 << 20   # the calibration copy reads and writes this many bytes
 FWD_KERNEL = re.compile(r"sparse_mla_fwd(_ws)?_kernel")   # the forward kernels' names
+BWD_KERNEL = re.compile(r"sparse_mla_bwd_kernel")         # the backward kernel's name
 
 
 def copy_calibration(dev, reps: int = 3):
@@ -84,7 +90,7 @@ def copy_calibration(dev, reps: int = 3):
     del src, dst
 
 
-def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: str):
+def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: str, op: str = "fwd"):
     """Turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE, in
     KiB per dispatch) into HBM bytes per forward launch, each scaled by what
     the same counter reads for the calibration copy, and store the result
@@ -106,19 +112,20 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: st
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         vals = per_dispatch(path, counter)
         copy = [v for (d, k), v in vals.items() if "neg" in k]
-        fwd = [v for (d, k), v in vals.items() if FWD_KERNEL.search(k)]
+        kern = FWD_KERNEL if op == "fwd" else BWD_KERNEL
+        fwd = [v for (d, k), v in vals.items() if kern.search(k)]
         if not copy or not fwd:
             raise SystemExit(f"{path}: no calibration copy or forward dispatch with {counter}")
         factor = COPY_BYTES / (statistics.median(copy) * 1024.0)
         fwd_bytes = statistics.median(fwd) * 1024.0 * factor
         tag = counter.split("_")[0].lower()
         out[f"{tag}_kib_copy"] = statistics.median(copy)
-        out[f"{tag}_kib_fwd"] = statistics.median(fwd)
+        out[f"{tag}_kib_kernel"] = statistics.median(fwd)
         out[f"{tag}_factor"] = round(factor, 4)
         out[f"{tag}_bytes"] = round(fwd_bytes)
         out[f"{tag}_dispatches"] = len(fwd)
     out["bytes_per_launch"] = out["fetch_bytes"] + out["write_bytes"]
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = traffic_path(workload, op)
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -249,7 +256,7 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_traffic:
-        summarize_traffic(args.workload, *args.summarize_traffic, args.traffic_command)
+        summarize_traffic(args.workload, *args.summarize_traffic, args.traffic_command, args.op)
         return
 
     if args.gpus != 1:
@@ -363,8 +370,8 @@ def main():
                 "unit": "TFLOP/s", "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic_for(args.workload)}
 
-    if args.op == "bwd" and roof["traffic"] is not None:
-        roof["traffic"] = None   # the stored counters are the forward's
+    if args.op == "bwd":
+        roof["traffic"] = traffic_for(args.workload, "bwd")
     rec = {
         "metric": METRIC if args.op == "fwd" else BWD_METRIC,
         "value": round(gbps, 2),
