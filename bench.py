@@ -90,7 +90,8 @@ def copy_calibration(dev, reps: int = 3):
     del src, dst
 
 
-def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: str, op: str = "fwd"):
+def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: str, op: str = "fwd",
+                      out_path: str | None = None):
     """Turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE, in
     KiB per dispatch) into HBM bytes per forward launch, each scaled by what
     the same counter reads for the calibration copy, and store the result
@@ -125,7 +126,7 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: st
         out[f"{tag}_bytes"] = round(fwd_bytes)
         out[f"{tag}_dispatches"] = len(fwd)
     out["bytes_per_launch"] = out["fetch_bytes"] + out["write_bytes"]
-    path = traffic_path(workload, op)
+    path = out_path or traffic_path(workload, op)
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")

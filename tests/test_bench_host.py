@@ -1,0 +1,68 @@
+"""Host-side checks of the measurement tooling in bench.py (no GPU needed)."""
+from __future__ import annotations
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for disp, kern, val in rows:
+            w.writerow({"Dispatch_Id": disp, "Kernel_Name": kern, "Counter_Name": counter, "Counter_Value": val})
+
+
+def test_traffic_summary_scales_by_the_copy(tmp_path):
+    copy_kib = bench.COPY_BYTES / 1024
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    # the copy reads COPY_BYTES but FETCH_SIZE shows half of it: fetch factor 2
+    _counter_csv(fetch, "FETCH_SIZE", [
+        (1, "void at::native::neg_kernel", copy_kib / 2),
+        (2, "void dsa::sparse_mla_fwd_kernel<1, false>(dsa::FwdArgs)", 1000.0),
+        (3, "void dsa::sparse_mla_fwd_kernel<1, false>(dsa::FwdArgs)", 1000.0),
+        (4, "dsa::sparse_mla_bwd_kernel<1>(dsa::BwdArgs)", 77.0)])
+    _counter_csv(write, "WRITE_SIZE", [
+        (1, "void at::native::neg_kernel", copy_kib),
+        (2, "void dsa::sparse_mla_fwd_kernel<1, false>(dsa::FwdArgs)", 300.0),
+        (3, "void dsa::sparse_mla_fwd_kernel<1, false>(dsa::FwdArgs)", 300.0)])
+    out = tmp_path / "t.json"
+    bench.summarize_traffic("swe", str(fetch), str(write), "cmd", op="fwd", out_path=str(out))
+    rec = json.loads(out.read_text())
+    assert rec["fetch_factor"] == 2.0 and rec["write_factor"] == 1.0
+    assert rec["fetch_bytes"] == 2 * 1000 * 1024 and rec["write_bytes"] == 300 * 1024
+    assert rec["bytes_per_launch"] == rec["fetch_bytes"] + rec["write_bytes"]
+    assert rec["fetch_dispatches"] == 2 and rec["source_hash"] == bench.source_hash()
+
+
+def test_valid_keys_flat_and_paged():
+    idx = torch.tensor([[0, 3, -1, 7], [9, -5, 2, 2]], dtype=torch.int32)
+    d = {"kv": torch.zeros((8, 576)), "indices": idx}
+    assert bench.valid_keys(d) == 5          # 0, 3, 7 | 2, 2 (9 and -5 are not rows)
+    d = {"kv_pages": torch.zeros((2, 4, 576)), "indices": idx, "q_per_seq": 1,
+         "seq_lens": torch.tensor([8, 3], dtype=torch.int32)}
+    assert bench.valid_keys(d) == 5          # seq 0 holds 8: 0, 3, 7 | seq 1 holds 3: 2, 2
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2 and "one GPU" in res.stderr
+
+
+def test_flop_and_byte_constants():
+    assert bench.FLOP_PER_KEY_HEAD == 2 * (576 + 512)
+    assert bench.ROW_BYTES == 1152
+    assert bench.BWD_FLOP_PER_KEY_HEAD == 2 * (3 * 576 + 2 * 512)
+    assert bench.BWD_BYTES_PER_KEY == 1152 + 576 * 4
+    assert np.isclose(bench.HBM_PEAK_GBPS, 8000.0) and np.isclose(bench.MFMA_BF16_PEAK_TFLOPS, 2500.0)
