@@ -61,6 +61,7 @@ struct BwdArgs {
   float* dkv;              // fp32 [N, 576], zeroed before this kernel
   int64_t dkv_st;
   int32_t head_blocks;     // workgroups per token (16 heads each)
+  const uint32_t* only;    // if set, tokens with only[t] == 0 are skipped (done by the kv-major pass)
 };
 
 constexpr int kBwPitch = 1168;                  // LDS row pitch of K rows and Q rows: 1152 + 16
@@ -97,6 +98,7 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
   const int n = lane & 15, g = lane >> 4;   // MFMA column / k-group of the lane
   const int64_t token = blockIdx.x / a.head_blocks;
   const int h0 = (int)(blockIdx.x % a.head_blocks) * HB;
+  if (a.only && a.only[token] == 0) return;   // uniform over the workgroup
 
   // ---------------------------------------------------------------- per-token inputs
   // Q (HB x 576) and dO (HB x 512) of the head block into LDS; padded heads are 0.
@@ -327,6 +329,267 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
         if (h < a.num_heads) a.dq[token * a.dq_st + (int64_t)h * a.dq_sh + d] = dq_acc[ht][k][e];
       }
     }
+}
+
+// ==================================================================== kv-major pass
+// For few heads (<= 16) and index rows that name a large share of the kv rows
+// (causal prefill: token t names most of 0..t), the token-major kernel above
+// adds 576 floats to dkv per (token, key): the atomics, not the MFMAs, bound
+// it. The kv-major pass turns the loops around. A workgroup owns one block of
+// 32 kv rows and a chunk of 64 tokens; for every token of the chunk that names
+// rows of the block (a "pair") it runs the same three phases as one tile of
+// the token-major kernel, with the block's rows as the tile and the named rows
+// as its valid keys. dkv of the block accumulates in registers over the
+// chunk's pairs and is added once; dq takes the atomics instead, H x 576 per
+// pair. With 8 heads and dense causal rows that is ~4x fewer atomic adds.
+//
+// A prepass per token builds the occupancy masks (bit r % 32 of word r / 32:
+// row r named), D = dO . O per head, and zeroes the token's dq. A token whose
+// row names some kv row twice is left to the token-major kernel (its masks
+// stay 0 and only[t] = 1), so duplicates keep counting once per occurrence.
+
+constexpr int kKvChunk = 64;        // tokens per kv-major workgroup (one wave's ballot)
+constexpr int kKvMaxWords = 8192;   // mask words per token row held in LDS (kv rows <= 262144)
+
+struct KvMajorArgs {
+  uint32_t* mask;     // u32 [num_words][num_tokens]: word w of token t at mask[w * T + t]
+  uint32_t* dup;      // u32 [num_tokens]: 1 = the row names a kv row twice
+  float* dbuf;        // fp32 [num_tokens][16]: D = dO . O per head (0 past num_heads)
+  int32_t num_words;  // ceil(num_kv / 32)
+};
+
+__global__ void __launch_bounds__(256)
+sparse_mla_bwd_prep_kernel(const BwdArgs a, const KvMajorArgs m) {
+  __shared__ uint32_t s_bm[kKvMaxWords];
+  __shared__ uint32_t s_dup;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t token = blockIdx.x;
+  for (int w = tid; w < m.num_words; w += 256) s_bm[w] = 0u;
+  if (tid == 0) s_dup = 0u;
+  __syncthreads();
+  const int32_t* row = a.idx + token * a.idx_st;
+  for (int j = tid; j < a.topk; j += 256) {
+    const int32_t v = row[j];
+    if (v >= 0 && (int64_t)v < a.num_kv) {
+      const uint32_t bit = 1u << (v & 31);
+      if (atomicOr(&s_bm[v >> 5], bit) & bit) s_dup = 1u;
+    }
+  }
+  // D per head (wave w: heads 4w .. 4w+3) and dq = 0 for this token
+  for (int hh = 0; hh < 4; ++hh) {
+    const int h = 4 * wave + hh;
+    float d = 0.f;
+    if (h < a.num_heads) {
+      const bf16x8_t o = *(const bf16x8_t*)(a.out + token * a.o_st + (int64_t)h * a.o_sh + 8 * lane);
+      const bf16x8_t dd = *(const bf16x8_t*)(a.dout + token * a.do_st + (int64_t)h * a.do_sh + 8 * lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d += (float)o[e] * (float)dd[e];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) d += __shfl_xor(d, off);
+    if (lane == 0) m.dbuf[token * 16 + h] = d;
+  }
+  for (int i = tid; i < a.num_heads * kDqk; i += 256)
+    a.dq[token * a.dq_st + (int64_t)(i / kDqk) * a.dq_sh + i % kDqk] = 0.f;
+  __syncthreads();
+  const uint32_t dup = s_dup;
+  if (tid == 0) m.dup[token] = dup;
+  for (int w = tid; w < m.num_words; w += 256) m.mask[(int64_t)w * a.num_tokens + token] = dup ? 0u : s_bm[w];
+}
+
+// One workgroup = (kv block b, token chunk c); blockIdx.x = c * num_words + b.
+__global__ void __launch_bounds__(256)
+sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
+  constexpr int HB = 16;
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[kBwStage];        // the block's 32 rows
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[2][HB * kBwPitch];    // pair's Q, double-buffered
+  __shared__ __attribute__((aligned(16))) uint8_t s_do[2][HB * kBwOPitch];  // pair's dO
+  __shared__ __attribute__((aligned(16))) float4_t s_dp[2][64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_pt[HB * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_dst[HB * 64];
+  __shared__ float s_D[2][HB], s_lse2[2][HB];
+  __shared__ int s_tok[kKvChunk];
+  __shared__ uint32_t s_msk[kKvChunk];
+  __shared__ int s_np;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int b = (int)(blockIdx.x % m.num_words);
+  const int64_t t0 = (int64_t)(blockIdx.x / m.num_words) * kKvChunk;
+  const int64_t r0 = (int64_t)b * kTileKeys;
+
+  // the chunk's tokens that name rows of this block, in token order
+  if (wave == 0) {
+    const int64_t t = t0 + lane;
+    const uint32_t w = t < a.num_tokens ? m.mask[(int64_t)b * a.num_tokens + t] : 0u;
+    const uint64_t act = __ballot(w != 0u);
+    if (w != 0u) {
+      const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(act >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)act, 0u));
+      s_tok[pos] = (int)lane;
+      s_msk[pos] = w;
+    }
+    if (lane == 0) s_np = __builtin_popcountll(act);
+  }
+  __syncthreads();
+  const int np = s_np;
+  if (np == 0) return;
+
+  // the block's rows (rows past num_kv are 0; their mask bits are never set)
+#pragma unroll
+  for (int k = 0; k < kBwGran; ++k) {
+    const int gi = tid + 256 * k, row = gi / (kDqk / 8), c = gi % (kDqk / 8);
+    bf16x8_t v = {};
+    if (r0 + row < a.num_kv) v = *(const bf16x8_t*)(a.kv + (r0 + row) * a.kv_st + 8 * c);
+    *(bf16x8_t*)(s_stage + row * kBwPitch + 16 * c) = v;
+  }
+
+  // Q (16 heads x 72 granules) and dO (16 x 64) of pair p: thread tid holds granules tid + 256k
+  constexpr int kPairGran = (HB * (kDqk / 8) + HB * (kDv / 8) + 255) / 256;   // 9
+  bf16x8_t preg[kPairGran];
+  float pl2 = 0.f, pD = 0.f;
+  auto load_pair = [&](int p) {
+    const int64_t t = t0 + s_tok[p];
+#pragma unroll
+    for (int k = 0; k < kPairGran; ++k) {
+      const int gi = tid + 256 * k;
+      bf16x8_t v = {};
+      if (gi < HB * (kDqk / 8)) {
+        const int h = gi / (kDqk / 8), c = gi % (kDqk / 8);
+        if (h < a.num_heads) v = *(const bf16x8_t*)(a.q + t * a.q_st + (int64_t)h * a.q_sh + 8 * c);
+      } else if (gi < HB * (kDqk / 8) + HB * (kDv / 8)) {
+        const int gj = gi - HB * (kDqk / 8), h = gj / (kDv / 8), c = gj % (kDv / 8);
+        if (h < a.num_heads) v = *(const bf16x8_t*)(a.dout + t * a.do_st + (int64_t)h * a.do_sh + 8 * c);
+      }
+      preg[k] = v;
+    }
+    if (tid < HB) {
+      // padded heads: +inf, so their P = exp2(score - inf) = 0
+      pl2 = tid < a.num_heads ? a.lse[t * a.lse_st + tid] * 1.4426950408889634f : INFINITY;
+      pD = m.dbuf[t * 16 + tid];
+    }
+  };
+  auto store_pair = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < kPairGran; ++k) {
+      const int gi = tid + 256 * k;
+      if (gi < HB * (kDqk / 8)) {
+        const int h = gi / (kDqk / 8), c = gi % (kDqk / 8);
+        *(bf16x8_t*)(s_q[buf] + h * kBwPitch + 16 * c) = preg[k];
+      } else if (gi < HB * (kDqk / 8) + HB * (kDv / 8)) {
+        const int gj = gi - HB * (kDqk / 8), h = gj / (kDv / 8), c = gj % (kDv / 8);
+        *(bf16x8_t*)(s_do[buf] + h * kBwOPitch + 16 * c) = preg[k];
+      }
+    }
+    if (tid < HB) {
+      s_lse2[buf][tid] = pl2;
+      s_D[buf][tid] = pD;
+    }
+  };
+  load_pair(0);
+  store_pair(0);
+  __syncthreads();
+
+  // K (waves 0, 1) or V (waves 2, 3) rows of key block kb as the MFMA A operand:
+  // lane holds key kb*16 + n, columns 32c + 8g .. +7
+  const bool s_role = wave < 2;
+  const int kb = wave & 1;
+  bf16x8_t areg[kDqk / 32];
+#pragma unroll
+  for (int c = 0; c < kDqk / 32; ++c)
+    areg[c] = (s_role || c < kDv / 32) ? lds16(s_stage + (kb * 16 + n) * kBwPitch + 64 * c + 16 * g) : (bf16x8_t){};
+
+  // dkv of key block kb2 = w >> 1, column tiles 18(w & 1) .. +17: lane holds
+  // column 16dt + n of keys kb2*16 + 4g .. +3
+  const int kb2 = wave >> 1;
+  float4_t dkv_acc[18];
+#pragma unroll
+  for (int k = 0; k < 18; ++k) dkv_acc[k] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  for (int p = 0; p < np; ++p) {
+    const int buf = p & 1;
+    if (p + 1 < np) load_pair(p + 1);   // in flight during the three phases
+    const int64_t t = t0 + s_tok[p];
+    const uint32_t msk = s_msk[p];
+    const uint8_t* sq = s_q[buf];
+    const uint8_t* sd = s_do[buf];
+
+    // ---- phase 1: S^T (waves 0, 1) or dP^T (waves 2, 3) of key block kb, 16 heads
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    if (s_role) {
+#pragma unroll
+      for (int c = 0; c < kDqk / 32; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(areg[c], lds16(sq + n * kBwPitch + 64 * c + 16 * g), acc, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int c = 0; c < kDv / 32; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(areg[c], lds16(sd + n * kBwOPitch + 64 * c + 16 * g), acc, 0, 0, 0);
+      s_dp[kb][lane] = acc;
+    }
+    __syncthreads();
+
+    // ---- phase 2: P and s*dS (lane: head n, keys kb*16 + 4g + e), masked by the pair's rows
+    if (s_role) {
+      const float4_t dp = s_dp[kb][lane];
+      const float Dh = s_D[buf][n], l2 = s_lse2[buf][n];
+      float pv[4], ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = (msk >> (kb * 16 + 4 * g + e)) & 1u;
+        pv[e] = ok ? __builtin_amdgcn_exp2f(acc[e] * a.scale_log2 - l2) : 0.f;
+        ds[e] = pv[e] * (dp[e] - Dh) * a.scale;
+      }
+      const int off = n * 64 + 2 * (kb * 16 + 4 * g);
+      *(uint2*)(s_pt + off) = (uint2){pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+      *(uint2*)(s_dst + off) = (uint2){pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
+    }
+    __syncthreads();
+
+    // ---- phase 3a: dq tiles 9w .. 9w+8 of token t += (s dS) K, added with atomics
+    {
+      const uint8_t* kt = s_stage + (8 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
+      const bf16x8_t ads = lds16(s_dst + n * 64 + 16 * g);
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        const int d0 = 16 * (9 * wave + k);
+        const bf16x8_t bk = join4(lds_read_tr16(kt + 2 * d0), lds_read_tr16(kt + 4 * kBwPitch + 2 * d0));
+        const float4_t c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads, bk, (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int h = 4 * g + e;
+          if (h < a.num_heads) unsafeAtomicAdd(a.dq + t * a.dq_st + (int64_t)h * a.dq_sh + d0 + n, c[e]);
+        }
+      }
+    }
+    // ---- phase 3b: dkv of the block += (s dS)^T Q + P^T dO over the 16 heads (registers)
+    {
+      const int aoff = (4 * g + (n >> 2)) * 64 + 2 * (kb2 * 16 + 4 * (n & 3));
+      const short4_t ads = lds_read_tr16(s_dst + aoff);
+      const short4_t ap = lds_read_tr16(s_pt + aoff);
+      const uint8_t* bq = sq + (4 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
+      const uint8_t* bo = sd + (4 * g + (n >> 2)) * kBwOPitch + 8 * (n & 3);
+#pragma unroll
+      for (int k = 0; k < 18; ++k) {
+        const int d0 = 16 * (18 * (wave & 1) + k);
+        dkv_acc[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ads, lds_read_tr16(bq + 2 * d0), dkv_acc[k], 0, 0, 0);
+        if (d0 < kDv) dkv_acc[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap, lds_read_tr16(bo + 2 * d0), dkv_acc[k], 0, 0, 0);
+      }
+    }
+    if (p + 1 < np) store_pair(buf ^ 1);   // the other buffer: last read before the previous pair's barrier
+    __syncthreads();
+  }
+
+  // ---- the block's dkv, once per workgroup (other chunks add to the same rows)
+#pragma unroll
+  for (int k = 0; k < 18; ++k) {
+    const int d0 = 16 * (18 * (wave & 1) + k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t r = r0 + kb2 * 16 + 4 * g + e;
+      if (r < a.num_kv) unsafeAtomicAdd(a.dkv + r * a.dkv_st + d0 + n, dkv_acc[k][e]);
+    }
+  }
 }
 
 // dkv = 0 before the backward accumulates into it: one thread per float4.

@@ -50,6 +50,7 @@ int current_device_cus() {
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 // Split choice. Each workgroup gathers at most kSegment entries. With few
 // tokens and long rows, more workgroups per token fill the 256 CUs; short
@@ -415,6 +416,36 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
   a.head_blocks = (num_heads + hb - 1) / hb;
   const int64_t wgs = num_tokens * a.head_blocks;
   if (wgs >= ((int64_t)1 << 31)) return DSA_ERR_UNSUPPORTED;
+
+  // kv-major pass when it adds fewer floats atomically than the token-major
+  // kernel: per (token, 32-row block) pair it adds H x 576 to dq where the
+  // token-major kernel adds 576 per named row, so it pays when a pair holds
+  // well over H named rows. The shapes stand in for that density: topk at
+  // least 3/64 of H x num_kv.
+  const int64_t words = (num_kv + 31) / 32;
+  const int64_t chunks = (num_tokens + dsa::kKvChunk - 1) / dsa::kKvChunk;
+  const int64_t mask_bytes = words * num_tokens * 4;
+  const int64_t ws_bytes = round_up(mask_bytes, 256) + round_up(num_tokens * 4, 256) + num_tokens * 16 * 4;
+  const bool kv_major = num_heads <= 16 && num_kv > 0 && words <= dsa::kKvMaxWords &&
+                        3 * num_kv * num_heads <= 64 * (int64_t)topk && ws_bytes <= ((int64_t)1 << 30) &&
+                        words * chunks < ((int64_t)1 << 31);
+  void* ws = nullptr;
+  if (kv_major && hipMallocAsync(&ws, (size_t)ws_bytes, s) == hipSuccess && ws) {
+    dsa::KvMajorArgs m;
+    m.mask = static_cast<uint32_t*>(ws);
+    m.dup = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + round_up(mask_bytes, 256));
+    m.dbuf = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(mask_bytes, 256) +
+                                      round_up(num_tokens * 4, 256));
+    m.num_words = (int32_t)words;
+    hipLaunchKernelGGL(dsa::sparse_mla_bwd_prep_kernel, dim3((unsigned)num_tokens), dim3(256), 0, s, a, m);
+    hipLaunchKernelGGL(dsa::sparse_mla_bwd_kv_kernel, dim3((unsigned)(words * chunks)), dim3(256), 0, s, a, m);
+    a.only = m.dup;   // rows with a repeated entry: token-major
+    hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, s, a);
+    const bool launched = hipGetLastError() == hipSuccess;
+    const bool freed = hipFreeAsync(ws, s) == hipSuccess;
+    return launched && freed ? DSA_OK : DSA_ERR_HIP;
+  }
+  (void)hipGetLastError();   // a failed stream-ordered allocation: token-major below
   if (hb == 16)
     hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, s, a);
   else

@@ -182,6 +182,19 @@ int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stri
  *          16-byte aligned, dkv_stride_row a multiple of 4 and >= 576.
  * stream   hipStream_t to enqueue on.
  *
+ * Two schedules, chosen from the sizes alone. Token-major: one workgroup per
+ * token and head block adds each named row's gradient into dkv. kv-major,
+ * when num_heads <= 16, 0 < num_kv <= 262144 and 3 * num_kv * num_heads <=
+ * 64 * topk (rows that name a large share of kv, as in causal prefill): one
+ * workgroup per (32-row kv block, 64-token chunk) keeps the block's dkv in
+ * registers and adds dq with atomics instead, so dq too may then differ in
+ * the last bits between calls. Tokens whose row names some kv row twice go
+ * to the token-major kernel within the same call. The kv-major schedule takes
+ * ceil(num_kv/32) * num_tokens * 4 + ~68 * num_tokens bytes of scratch from
+ * the device's default memory pool, stream-ordered (hipMallocAsync, freed with
+ * hipFreeAsync on the same stream); if that allocation fails, or the scratch
+ * would exceed 1 GiB, the call takes the token-major schedule.
+ *
  * Limits: 1 <= num_heads <= 128, 1 <= topk <= 65536. dq and dkv must not
  * overlap the inputs or each other (checked on the host: DSA_ERR_INVALID_ARGUMENT).
  */

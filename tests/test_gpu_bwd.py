@@ -77,6 +77,13 @@ def run(q, kv, idx, sm, dout, own_forward=False):
     return dq, dkv
 
 
+def kv_major(H, N, topk):
+    """The library's choice of the kv-major pass (stated with the backward in
+    include/dsa_sparse_mla.h): at most 16 heads, at most 262144 kv rows, and
+    topk at least 3/64 of H x num_kv."""
+    return H <= 16 and 0 < N <= 32 * 8192 and 3 * N * H <= 64 * topk
+
+
 def ref(q, kv, idx, sm, dout):
     return sparse_mla_bwd_ref(np64(q), np64(kv), idx.cpu().numpy(), sm, np64(dout))
 
@@ -204,3 +211,52 @@ def test_bwd_strided_and_many_heads():
     rdq, rdkv = ref(q, kv, idx, 1 / 24, dout)
     check_grad(np64(dq), rdq, "dq strided H=128")
     check_grad(np64(dkv), rdkv, "dkv strided H=128")
+
+
+@pytest.mark.parametrize("H", [1, 5, 8, 16])
+def test_bwd_kv_major_pass(H):
+    """The kv-major pass: 150 tokens (three 64-token chunks, the last ragged),
+    200 kv rows (seven 32-row blocks, the last with 8 rows), distinct entries
+    with -1 and out-of-range values; a token with no key, a token with only
+    out-of-range values, and two tokens that name a row twice (those two go
+    to the token-major kernel inside the same call)."""
+    T, N, topk = 150, 200, 160
+    assert kv_major(H, N, topk)
+    q, kv, idx, dout = random_case(T, H, N, topk, seed=300 + H, dup=False)
+    idx[4] = -1
+    idx[9] = 213
+    idx[40, 0] = idx[40, 1] = 17           # duplicate pair
+    idx[141, 5] = idx[141, 100] = 199      # duplicate of the last row
+    dq, dkv = run(q, kv, idx, 1 / 24, dout)
+    dq, dkv = np64(dq), np64(dkv)
+    assert np.all(dq[4] == 0) and np.all(dq[9] == 0)
+    named = set(int(v) for v in idx.numpy().ravel() if 0 <= v < N)
+    untouched = [r for r in range(N) if r not in named]
+    assert np.all(dkv[untouched] == 0)
+    rdq, rdkv = ref(q, kv, idx, 1 / 24, dout)
+    check_grad(dq, rdq, f"dq kv-major H={H}")
+    check_grad(dkv, rdkv, f"dkv kv-major H={H}")
+
+
+def test_bwd_kv_major_causal_rows():
+    """Dense causal rows (token t names 0..t in shuffled order): every pair of
+    the lower triangle, blocks named by one token only at the diagonal."""
+    d = workloads.make_flat("swe", num_tokens=333, topk=512)
+    T, H = d["q"].shape[:2]
+    N = d["kv"].shape[0]
+    assert kv_major(H, N, 512)
+    g = torch.Generator().manual_seed(12)
+    dout = torch.randn((T, H, 512), generator=g).to(torch.bfloat16)
+    dq, dkv = run(d["q"], d["kv"], d["indices"], d["sm_scale"], dout)
+    rdq, rdkv = ref(d["q"], d["kv"], d["indices"], d["sm_scale"], dout)
+    check_grad(np64(dq), rdq, "dq causal kv-major")
+    check_grad(np64(dkv), rdkv, "dkv causal kv-major")
+
+
+def test_bwd_paths_of_the_cases():
+    """The cases above reach both kernels: the token-major one at 8+ heads
+    with sparse rows, the kv-major pass for the SWE-like rows."""
+    assert not kv_major(8, 300, 100) and kv_major(1, 300, 100)
+    d = workloads.make_flat("swe")
+    assert kv_major(d["q"].shape[1], d["kv"].shape[0], d["indices"].shape[1])
+    assert not kv_major(64, 300, 100)
