@@ -9,8 +9,9 @@ dqk 576 / dv 512, topk 2048, bf16 (the shape of "feat: add XTuner TileLang
 sparse MLA backend", Performance > Isolated sparse MLA forward).
 
 With --op bwd it times the backward instead (flat workloads): one step is
-the dkv zero fill and the backward kernel, after one forward that supplies
-out and LSE; `value` then counts 3456 bytes per valid key (the 1152-byte
+one backward call (the dkv zero fill, then the token-major kernel, or the
+kv-major prepass and pass with the token-major kernel for rows that repeat
+an entry), after one forward that supplies out and LSE; `value` then counts 3456 bytes per valid key (the 1152-byte
 gathered row and its 2304-byte fp32 dkv addition) and `tflops` 5504 flops
 per valid key and head.
 
@@ -75,7 +76,10 @@ def traffic_for(workload: str, op: str = "fwd"):
 
 COPY_BYTES = 256 << 20   # the calibration copy reads and writes this many bytes
 FWD_KERNEL = re.compile(r"sparse_mla_fwd(_ws)?_kernel")   # the forward kernels' names
-BWD_KERNEL = re.compile(r"sparse_mla_bwd_kernel")         # the backward kernel's name
+# the kernels of one backward call: the dkv fill (once per call), the kv-major
+# prepass and pass, and the token-major kernel
+BWD_KERNEL = re.compile(r"dkv_zero_kernel|sparse_mla_bwd_(prep_|kv_)?kernel")
+BWD_CALL_MARK = re.compile(r"dkv_zero_kernel")
 
 
 def copy_calibration(dev, reps: int = 3):
@@ -116,15 +120,21 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: st
         kern = FWD_KERNEL if op == "fwd" else BWD_KERNEL
         fwd = [v for (d, k), v in vals.items() if kern.search(k)]
         if not copy or not fwd:
-            raise SystemExit(f"{path}: no calibration copy or forward dispatch with {counter}")
+            raise SystemExit(f"{path}: no calibration copy or {op} dispatch with {counter}")
         factor = COPY_BYTES / (statistics.median(copy) * 1024.0)
-        fwd_bytes = statistics.median(fwd) * 1024.0 * factor
+        if op == "fwd":
+            # one forward kernel per launch: the median dispatch
+            kib, count = statistics.median(fwd), len(fwd)
+        else:
+            # a backward call launches several kernels: their sum per call
+            count = sum(1 for (d, k) in vals if BWD_CALL_MARK.search(k))
+            kib = sum(fwd) / max(count, 1)
         tag = counter.split("_")[0].lower()
         out[f"{tag}_kib_copy"] = statistics.median(copy)
-        out[f"{tag}_kib_kernel"] = statistics.median(fwd)
+        out[f"{tag}_kib_kernel"] = kib
         out[f"{tag}_factor"] = round(factor, 4)
-        out[f"{tag}_bytes"] = round(fwd_bytes)
-        out[f"{tag}_dispatches"] = len(fwd)
+        out[f"{tag}_bytes"] = round(kib * 1024.0 * factor)
+        out[f"{tag}_dispatches"] = count
     out["bytes_per_launch"] = out["fetch_bytes"] + out["write_bytes"]
     path = out_path or traffic_path(workload, op)
     with open(path, "w") as f:

@@ -398,7 +398,9 @@ sparse_mla_bwd_prep_kernel(const BwdArgs a, const KvMajorArgs m) {
 }
 
 // One workgroup = (kv block b, token chunk c); blockIdx.x = c * num_words + b.
-__global__ void __launch_bounds__(256)
+// Its LDS allows one workgroup per CU, so the compiler may use the whole
+// register file (one wave per SIMD) to keep operand reads in flight.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
   constexpr int HB = 16;
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[kBwStage];        // the block's 32 rows
@@ -464,9 +466,8 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
       }
       preg[k] = v;
     }
-    if (tid < HB) {
-      // padded heads: +inf, so their P = exp2(score - inf) = 0
-      pl2 = tid < a.num_heads ? a.lse[t * a.lse_st + tid] * 1.4426950408889634f : INFINITY;
+    if (tid < HB && tid < a.num_heads) {
+      pl2 = a.lse[t * a.lse_st + tid];   // scaled when stored: no wait on the loads here
       pD = m.dbuf[t * 16 + tid];
     }
   };
@@ -483,8 +484,9 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
       }
     }
     if (tid < HB) {
-      s_lse2[buf][tid] = pl2;
-      s_D[buf][tid] = pD;
+      // padded heads: +inf, so their P = exp2(score - inf) = 0
+      s_lse2[buf][tid] = tid < a.num_heads ? pl2 * 1.4426950408889634f : INFINITY;
+      s_D[buf][tid] = tid < a.num_heads ? pD : 0.f;
     }
   };
   load_pair(0);
@@ -546,23 +548,33 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
     }
     __syncthreads();
 
-    // ---- phase 3a: dq tiles 9w .. 9w+8 of token t += (s dS) K, added with atomics
+    // ---- phase 3a: dq tiles 9w .. 9w+8 of token t += (s dS) K, added with
+    // atomics. All operand reads are issued before the first product.
     {
       const uint8_t* kt = s_stage + (8 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
       const bf16x8_t ads = lds16(s_dst + n * 64 + 16 * g);
+      bf16x8_t bk[9];
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
         const int d0 = 16 * (9 * wave + k);
-        const bf16x8_t bk = join4(lds_read_tr16(kt + 2 * d0), lds_read_tr16(kt + 4 * kBwPitch + 2 * d0));
-        const float4_t c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads, bk, (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int h = 4 * g + e;
-          if (h < a.num_heads) unsafeAtomicAdd(a.dq + t * a.dq_st + (int64_t)h * a.dq_sh + d0 + n, c[e]);
-        }
+        bk[k] = join4(lds_read_tr16(kt + 2 * d0), lds_read_tr16(kt + 4 * kBwPitch + 2 * d0));
       }
+      float4_t c[9];
+#pragma unroll
+      for (int k = 0; k < 9; ++k)
+        c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads, bk[k], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      // lanes of heads past num_heads add nothing (lane group g holds heads 4g .. 4g+3)
+      const int hv = a.num_heads - 4 * g;
+      float* dqt = a.dq + t * a.dq_st + (int64_t)(4 * g) * a.dq_sh + n;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < hv) {
+#pragma unroll
+          for (int k = 0; k < 9; ++k) unsafeAtomicAdd(dqt + (int64_t)e * a.dq_sh + 16 * (9 * wave + k), c[k][e]);
+        }
     }
-    // ---- phase 3b: dkv of the block += (s dS)^T Q + P^T dO over the 16 heads (registers)
+    // ---- phase 3b: dkv of the block += (s dS)^T Q + P^T dO over the 16 heads (registers),
+    // operands read in two halves of 9 column tiles ahead of their products
     {
       const int aoff = (4 * g + (n >> 2)) * 64 + 2 * (kb2 * 16 + 4 * (n & 3));
       const short4_t ads = lds_read_tr16(s_dst + aoff);
@@ -570,10 +582,21 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
       const uint8_t* bq = sq + (4 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
       const uint8_t* bo = sd + (4 * g + (n >> 2)) * kBwOPitch + 8 * (n & 3);
 #pragma unroll
-      for (int k = 0; k < 18; ++k) {
-        const int d0 = 16 * (18 * (wave & 1) + k);
-        dkv_acc[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ads, lds_read_tr16(bq + 2 * d0), dkv_acc[k], 0, 0, 0);
-        if (d0 < kDv) dkv_acc[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap, lds_read_tr16(bo + 2 * d0), dkv_acc[k], 0, 0, 0);
+      for (int half = 0; half < 2; ++half) {
+        short4_t oq[9], oo[9];
+#pragma unroll
+        for (int k = 0; k < 9; ++k) {
+          const int d0 = 16 * (18 * (wave & 1) + 9 * half + k);
+          oq[k] = lds_read_tr16(bq + 2 * d0);
+          oo[k] = d0 < kDv ? lds_read_tr16(bo + 2 * d0) : (short4_t){};
+        }
+#pragma unroll
+        for (int k = 0; k < 9; ++k) {
+          const int d0 = 16 * (18 * (wave & 1) + 9 * half + k);
+          float4_t& acc2 = dkv_acc[9 * half + k];
+          acc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ads, oq[k], acc2, 0, 0, 0);
+          if (d0 < kDv) acc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap, oo[k], acc2, 0, 0, 0);
+        }
       }
     }
     if (p + 1 < np) store_pair(buf ^ 1);   // the other buffer: last read before the previous pair's barrier

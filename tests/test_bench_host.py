@@ -45,6 +45,25 @@ def test_traffic_summary_scales_by_the_copy(tmp_path):
     assert rec["fetch_dispatches"] == 2 and rec["source_hash"] == bench.source_hash()
 
 
+def test_backward_traffic_sums_the_kernels_of_a_call(tmp_path):
+    copy_kib = bench.COPY_BYTES / 1024
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    call = [("void dsa::dkv_zero_kernel(float*, long, long)", 1.0),
+            ("void dsa::sparse_mla_bwd_prep_kernel(dsa::BwdArgs, dsa::KvMajorArgs)", 10.0),
+            ("void dsa::sparse_mla_bwd_kv_kernel(dsa::BwdArgs, dsa::KvMajorArgs)", 100.0),
+            ("void dsa::sparse_mla_bwd_kernel<1>(dsa::BwdArgs)", 5.0)]
+    rows = [(1, "void at::native::neg_kernel", copy_kib / 2),
+            (2, "void dsa::sparse_mla_fwd_kernel<1, false>(dsa::FwdArgs)", 999.0)]
+    rows += [(3 + 4 * c + i, k, v) for c in range(2) for i, (k, v) in enumerate(call)]
+    _counter_csv(fetch, "FETCH_SIZE", rows)
+    _counter_csv(write, "WRITE_SIZE", [(d, k, 2 * v if "neg" not in k else copy_kib) for d, k, v in rows])
+    out = tmp_path / "t.json"
+    bench.summarize_traffic("swe", str(fetch), str(write), "cmd", op="bwd", out_path=str(out))
+    rec = json.loads(out.read_text())
+    assert rec["fetch_dispatches"] == 2 and rec["fetch_kib_kernel"] == 116.0
+    assert rec["fetch_bytes"] == 2 * 116 * 1024 and rec["write_bytes"] == 232 * 1024
+
+
 def test_valid_keys_flat_and_paged():
     idx = torch.tensor([[0, 3, -1, 7], [9, -5, 2, 2]], dtype=torch.int32)
     d = {"kv": torch.zeros((8, 576)), "indices": idx}
