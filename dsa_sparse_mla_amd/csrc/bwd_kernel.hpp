@@ -336,12 +336,14 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
 // (causal prefill: token t names most of 0..t), the token-major kernel above
 // adds 576 floats to dkv per (token, key): the atomics, not the MFMAs, bound
 // it. The kv-major pass turns the loops around. A workgroup owns one block of
-// 32 kv rows and a chunk of 64 tokens; for every token of the chunk that names
-// rows of the block (a "pair") it runs the same three phases as one tile of
-// the token-major kernel, with the block's rows as the tile and the named rows
-// as its valid keys. dkv of the block accumulates in registers over the
-// chunk's pairs and is added once; dq takes the atomics instead, H x 576 per
-// pair. With 8 heads and dense causal rows that is ~4x fewer atomic adds.
+// 32 kv rows and a chunk of 64 tokens. The chunk's tokens that name rows of
+// the block are taken in steps: each step runs the three phases of one tile
+// of the token-major kernel with the block's rows as the tile, the named rows
+// as its valid keys, and the 16 MFMA columns filled by 16 / hp tokens of hp
+// heads each (hp = num_heads rounded up to a power of two). dkv of the block
+// accumulates in registers over the chunk and is added once; dq takes the
+// atomics instead, num_heads x 576 per (token, block). With 8 heads and dense
+// causal rows that is ~4x fewer atomic adds.
 //
 // A prepass per token builds the occupancy masks (bit r % 32 of word r / 32:
 // row r named), D = dO . O per head, and zeroes the token's dq. A token whose
@@ -404,8 +406,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
   constexpr int HB = 16;
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[kBwStage];        // the block's 32 rows
-  __shared__ __attribute__((aligned(16))) uint8_t s_q[2][HB * kBwPitch];    // pair's Q, double-buffered
-  __shared__ __attribute__((aligned(16))) uint8_t s_do[2][HB * kBwOPitch];  // pair's dO
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[2][HB * kBwPitch];    // the step's Q columns, double-buffered
+  __shared__ __attribute__((aligned(16))) uint8_t s_do[2][HB * kBwOPitch];  // the step's dO columns
   __shared__ __attribute__((aligned(16))) float4_t s_dp[2][64];
   __shared__ __attribute__((aligned(16))) uint8_t s_pt[HB * 64];
   __shared__ __attribute__((aligned(16))) uint8_t s_dst[HB * 64];
@@ -422,7 +424,7 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
   const int64_t t0 = (int64_t)(blockIdx.x / m.num_words) * kKvChunk;
   const int64_t r0 = (int64_t)b * kTileKeys;
 
-  // the chunk's tokens that name rows of this block, in token order
+  // the chunk's tokens that name rows of this block, in token order (the token list)
   if (wave == 0) {
     const int64_t t = t0 + lane;
     const uint32_t w = t < a.num_tokens ? m.mask[(int64_t)b * a.num_tokens + t] : 0u;
@@ -437,6 +439,20 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
   __syncthreads();
   const int np = s_np;
   if (np == 0) return;
+  // The 16 MFMA columns ("heads" of the products) carry tpp tokens of the
+  // list at once, hp = 16 / tpp columns each (hp = num_heads rounded up to a
+  // power of two): column h is head h % hp of token entry p*tpp + h / hp.
+  // The dkv product then sums over those tokens too, and at 8 heads two
+  // tokens take the MFMA work that one did.
+  const int lhp = a.num_heads <= 1 ? 0 : 32 - __builtin_clz((unsigned)(a.num_heads - 1));
+  const int hp = 1 << lhp, tpp = 16 >> lhp;
+  const int nsteps = (np + tpp - 1) / tpp;
+  // token (or -1) and head of column h in step p
+  auto column = [&](int p, int h, int& hh) -> int64_t {
+    const int ti = p * tpp + (h >> lhp);
+    hh = h & (hp - 1);
+    return (ti < np && hh < a.num_heads) ? t0 + s_tok[ti] : (int64_t)-1;
+  };
 
   // the block's rows (rows past num_kv are 0; their mask bits are never set)
 #pragma unroll
@@ -447,31 +463,39 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
     *(bf16x8_t*)(s_stage + row * kBwPitch + 16 * c) = v;
   }
 
-  // Q (16 heads x 72 granules) and dO (16 x 64) of pair p: thread tid holds granules tid + 256k
+  // Q (16 columns x 72 granules) and dO (16 x 64) of step p: thread tid holds granules tid + 256k
   constexpr int kPairGran = (HB * (kDqk / 8) + HB * (kDv / 8) + 255) / 256;   // 9
   bf16x8_t preg[kPairGran];
   float pl2 = 0.f, pD = 0.f;
-  auto load_pair = [&](int p) {
-    const int64_t t = t0 + s_tok[p];
+  bool pok = false;
+  auto load_step = [&](int p) {
 #pragma unroll
     for (int k = 0; k < kPairGran; ++k) {
       const int gi = tid + 256 * k;
       bf16x8_t v = {};
+      int hh;
       if (gi < HB * (kDqk / 8)) {
         const int h = gi / (kDqk / 8), c = gi % (kDqk / 8);
-        if (h < a.num_heads) v = *(const bf16x8_t*)(a.q + t * a.q_st + (int64_t)h * a.q_sh + 8 * c);
+        const int64_t t = column(p, h, hh);
+        if (t >= 0) v = *(const bf16x8_t*)(a.q + t * a.q_st + (int64_t)hh * a.q_sh + 8 * c);
       } else if (gi < HB * (kDqk / 8) + HB * (kDv / 8)) {
         const int gj = gi - HB * (kDqk / 8), h = gj / (kDv / 8), c = gj % (kDv / 8);
-        if (h < a.num_heads) v = *(const bf16x8_t*)(a.dout + t * a.do_st + (int64_t)h * a.do_sh + 8 * c);
+        const int64_t t = column(p, h, hh);
+        if (t >= 0) v = *(const bf16x8_t*)(a.dout + t * a.do_st + (int64_t)hh * a.do_sh + 8 * c);
       }
       preg[k] = v;
     }
-    if (tid < HB && tid < a.num_heads) {
-      pl2 = a.lse[t * a.lse_st + tid];   // scaled when stored: no wait on the loads here
-      pD = m.dbuf[t * 16 + tid];
+    if (tid < HB) {
+      int hh;
+      const int64_t t = column(p, tid, hh);
+      pok = t >= 0;
+      if (pok) {
+        pl2 = a.lse[t * a.lse_st + hh];   // scaled when stored: no wait on the loads here
+        pD = m.dbuf[t * 16 + hh];
+      }
     }
   };
-  auto store_pair = [&](int buf) {
+  auto store_step = [&](int buf) {
 #pragma unroll
     for (int k = 0; k < kPairGran; ++k) {
       const int gi = tid + 256 * k;
@@ -484,13 +508,13 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
       }
     }
     if (tid < HB) {
-      // padded heads: +inf, so their P = exp2(score - inf) = 0
-      s_lse2[buf][tid] = tid < a.num_heads ? pl2 * 1.4426950408889634f : INFINITY;
-      s_D[buf][tid] = tid < a.num_heads ? pD : 0.f;
+      // empty columns: +inf, so their P = exp2(score - inf) = 0
+      s_lse2[buf][tid] = pok ? pl2 * 1.4426950408889634f : INFINITY;
+      s_D[buf][tid] = pok ? pD : 0.f;
     }
   };
-  load_pair(0);
-  store_pair(0);
+  load_step(0);
+  store_step(0);
   __syncthreads();
 
   // K (waves 0, 1) or V (waves 2, 3) rows of key block kb as the MFMA A operand:
@@ -509,11 +533,9 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
 #pragma unroll
   for (int k = 0; k < 18; ++k) dkv_acc[k] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  for (int p = 0; p < np; ++p) {
+  for (int p = 0; p < nsteps; ++p) {
     const int buf = p & 1;
-    if (p + 1 < np) load_pair(p + 1);   // in flight during the three phases
-    const int64_t t = t0 + s_tok[p];
-    const uint32_t msk = s_msk[p];
+    if (p + 1 < nsteps) load_step(p + 1);   // in flight during the three phases
     const uint8_t* sq = s_q[buf];
     const uint8_t* sd = s_do[buf];
 
@@ -531,8 +553,10 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
     }
     __syncthreads();
 
-    // ---- phase 2: P and s*dS (lane: head n, keys kb*16 + 4g + e), masked by the pair's rows
+    // ---- phase 2: P and s*dS (lane: head n, keys kb*16 + 4g + e), masked by each column's token's rows
     if (s_role) {
+      const int ti = p * tpp + (n >> lhp);   // the token entry of this lane's column
+      const uint32_t msk = ti < np ? s_msk[ti] : 0u;
       const float4_t dp = s_dp[kb][lane];
       const float Dh = s_D[buf][n], l2 = s_lse2[buf][n];
       float pv[4], ds[4];
@@ -548,8 +572,8 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
     }
     __syncthreads();
 
-    // ---- phase 3a: dq tiles 9w .. 9w+8 of token t += (s dS) K, added with
-    // atomics. All operand reads are issued before the first product.
+    // ---- phase 3a: dq tiles 9w .. 9w+8 of the step's tokens += (s dS) K, added
+    // with atomics. All operand reads are issued before the first product.
     {
       const uint8_t* kt = s_stage + (8 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
       const bf16x8_t ads = lds16(s_dst + n * 64 + 16 * g);
@@ -563,15 +587,17 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
 #pragma unroll
       for (int k = 0; k < 9; ++k)
         c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads, bk[k], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      // lanes of heads past num_heads add nothing (lane group g holds heads 4g .. 4g+3)
-      const int hv = a.num_heads - 4 * g;
-      float* dqt = a.dq + t * a.dq_st + (int64_t)(4 * g) * a.dq_sh + n;
+      // row 4g + e of the tile is column 4g + e of the step; empty columns add nothing
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (e < hv) {
+      for (int e = 0; e < 4; ++e) {
+        int hh;
+        const int64_t t = column(p, 4 * g + e, hh);
+        if (t >= 0) {
+          float* dqt = a.dq + t * a.dq_st + (int64_t)hh * a.dq_sh + n;
 #pragma unroll
-          for (int k = 0; k < 9; ++k) unsafeAtomicAdd(dqt + (int64_t)e * a.dq_sh + 16 * (9 * wave + k), c[k][e]);
+          for (int k = 0; k < 9; ++k) unsafeAtomicAdd(dqt + 16 * (9 * wave + k), c[k][e]);
         }
+      }
     }
     // ---- phase 3b: dkv of the block += (s dS)^T Q + P^T dO over the 16 heads (registers),
     // operands read in two halves of 9 column tiles ahead of their products
@@ -599,7 +625,7 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
         }
       }
     }
-    if (p + 1 < np) store_pair(buf ^ 1);   // the other buffer: last read before the previous pair's barrier
+    if (p + 1 < nsteps) store_step(buf ^ 1);   // the other buffer: last read before the previous step's barrier
     __syncthreads();
   }
 
