@@ -400,18 +400,19 @@ sparse_mla_bwd_prep_kernel(const BwdArgs a, const KvMajorArgs m) {
 }
 
 // One workgroup = (kv block b, token chunk c); blockIdx.x = c * num_words + b.
-// Its LDS allows one workgroup per CU, so the compiler may use the whole
-// register file (one wave per SIMD) to keep operand reads in flight.
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// Sized for two workgroups per CU (<= 80 KB of LDS, <= 256 registers per
+// lane), so that one workgroup's atomic and load waits overlap the other's
+// products.
+__global__ void __launch_bounds__(256, 2)
 sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
   constexpr int HB = 16;
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[kBwStage];        // the block's 32 rows
-  __shared__ __attribute__((aligned(16))) uint8_t s_q[2][HB * kBwPitch];    // the step's Q columns, double-buffered
-  __shared__ __attribute__((aligned(16))) uint8_t s_do[2][HB * kBwOPitch];  // the step's dO columns
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[1][HB * kBwPitch];    // the step's Q columns
+  __shared__ __attribute__((aligned(16))) uint8_t s_do[1][HB * kBwOPitch];  // the step's dO columns
   __shared__ __attribute__((aligned(16))) float4_t s_dp[2][64];
   __shared__ __attribute__((aligned(16))) uint8_t s_pt[HB * 64];
   __shared__ __attribute__((aligned(16))) uint8_t s_dst[HB * 64];
-  __shared__ float s_D[2][HB], s_lse2[2][HB];
+  __shared__ float s_D[1][HB], s_lse2[1][HB];
   __shared__ int s_tok[kKvChunk];
   __shared__ uint32_t s_msk[kKvChunk];
   __shared__ int s_np;
@@ -517,14 +518,11 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
   store_step(0);
   __syncthreads();
 
-  // K (waves 0, 1) or V (waves 2, 3) rows of key block kb as the MFMA A operand:
-  // lane holds key kb*16 + n, columns 32c + 8g .. +7
+  // K (waves 0, 1) or V (waves 2, 3) rows of key block kb are the MFMA A
+  // operand, read from the block's rows: lane holds key kb*16 + n, columns 32c + 8g .. +7
   const bool s_role = wave < 2;
   const int kb = wave & 1;
-  bf16x8_t areg[kDqk / 32];
-#pragma unroll
-  for (int c = 0; c < kDqk / 32; ++c)
-    areg[c] = (s_role || c < kDv / 32) ? lds16(s_stage + (kb * 16 + n) * kBwPitch + 64 * c + 16 * g) : (bf16x8_t){};
+  const uint8_t* arow = s_stage + (kb * 16 + n) * kBwPitch + 16 * g;
 
   // dkv of key block kb2 = w >> 1, column tiles 18(w & 1) .. +17: lane holds
   // column 16dt + n of keys kb2*16 + 4g .. +3
@@ -534,7 +532,7 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
   for (int k = 0; k < 18; ++k) dkv_acc[k] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
   for (int p = 0; p < nsteps; ++p) {
-    const int buf = p & 1;
+    const int buf = 0;
     if (p + 1 < nsteps) load_step(p + 1);   // in flight during the three phases
     const uint8_t* sq = s_q[buf];
     const uint8_t* sd = s_do[buf];
@@ -544,11 +542,11 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
     if (s_role) {
 #pragma unroll
       for (int c = 0; c < kDqk / 32; ++c)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(areg[c], lds16(sq + n * kBwPitch + 64 * c + 16 * g), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow + 64 * c), lds16(sq + n * kBwPitch + 64 * c + 16 * g), acc, 0, 0, 0);
     } else {
 #pragma unroll
       for (int c = 0; c < kDv / 32; ++c)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(areg[c], lds16(sd + n * kBwOPitch + 64 * c + 16 * g), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow + 64 * c), lds16(sd + n * kBwOPitch + 64 * c + 16 * g), acc, 0, 0, 0);
       s_dp[kb][lane] = acc;
     }
     __syncthreads();
@@ -577,16 +575,19 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
     {
       const uint8_t* kt = s_stage + (8 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
       const bf16x8_t ads = lds16(s_dst + n * 64 + 16 * g);
-      bf16x8_t bk[9];
-#pragma unroll
-      for (int k = 0; k < 9; ++k) {
-        const int d0 = 16 * (9 * wave + k);
-        bk[k] = join4(lds_read_tr16(kt + 2 * d0), lds_read_tr16(kt + 4 * kBwPitch + 2 * d0));
-      }
       float4_t c[9];
 #pragma unroll
-      for (int k = 0; k < 9; ++k)
-        c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads, bk[k], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      for (int k3 = 0; k3 < 9; k3 += 3) {
+        bf16x8_t bk[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          const int d0 = 16 * (9 * wave + k3 + k);
+          bk[k] = join4(lds_read_tr16(kt + 2 * d0), lds_read_tr16(kt + 4 * kBwPitch + 2 * d0));
+        }
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+          c[k3 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads, bk[k], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      }
       // row 4g + e of the tile is column 4g + e of the step; empty columns add nothing
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -608,25 +609,28 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
       const uint8_t* bq = sq + (4 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
       const uint8_t* bo = sd + (4 * g + (n >> 2)) * kBwOPitch + 8 * (n & 3);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        short4_t oq[9], oo[9];
+      for (int half = 0; half < 3; ++half) {
+        short4_t oq[6], oo[6];
 #pragma unroll
-        for (int k = 0; k < 9; ++k) {
-          const int d0 = 16 * (18 * (wave & 1) + 9 * half + k);
+        for (int k = 0; k < 6; ++k) {
+          const int d0 = 16 * (18 * (wave & 1) + 6 * half + k);
           oq[k] = lds_read_tr16(bq + 2 * d0);
           oo[k] = d0 < kDv ? lds_read_tr16(bo + 2 * d0) : (short4_t){};
         }
 #pragma unroll
-        for (int k = 0; k < 9; ++k) {
-          const int d0 = 16 * (18 * (wave & 1) + 9 * half + k);
-          float4_t& acc2 = dkv_acc[9 * half + k];
+        for (int k = 0; k < 6; ++k) {
+          const int d0 = 16 * (18 * (wave & 1) + 6 * half + k);
+          float4_t& acc2 = dkv_acc[6 * half + k];
           acc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ads, oq[k], acc2, 0, 0, 0);
           if (d0 < kDv) acc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap, oo[k], acc2, 0, 0, 0);
         }
       }
     }
-    if (p + 1 < nsteps) store_step(buf ^ 1);   // the other buffer: last read before the previous step's barrier
-    __syncthreads();
+    __syncthreads();   // every wave is done with this step's Q, dO, P and s*dS
+    if (p + 1 < nsteps) {
+      store_step(0);
+      __syncthreads();
+    }
   }
 
   // ---- the block's dkv, once per workgroup (other chunks add to the same rows)
