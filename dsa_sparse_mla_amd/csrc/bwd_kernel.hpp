@@ -335,15 +335,15 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
 // For few heads (<= 16) and index rows that name a large share of the kv rows
 // (causal prefill: token t names most of 0..t), the token-major kernel above
 // adds 576 floats to dkv per (token, key): the atomics, not the MFMAs, bound
-// it. The kv-major pass turns the loops around. A workgroup owns one block of
-// 32 kv rows and a chunk of 64 tokens. The chunk's tokens that name rows of
-// the block are taken in steps: each step runs the three phases of one tile
-// of the token-major kernel with the block's rows as the tile, the named rows
+// it. The kv-major pass turns the loops around. A workgroup owns two blocks
+// of 32 kv rows and a chunk of 64 tokens. The chunk's tokens that name rows
+// of the blocks are taken in steps: each step runs the three phases of one
+// tile of the token-major kernel with the 64 rows as the tile, the named rows
 // as its valid keys, and the 16 MFMA columns filled by 16 / hp tokens of hp
-// heads each (hp = num_heads rounded up to a power of two). dkv of the block
+// heads each (hp = num_heads rounded up to a power of two). dkv of the rows
 // accumulates in registers over the chunk and is added once; dq takes the
-// atomics instead, num_heads x 576 per (token, block). With 8 heads and dense
-// causal rows that is ~4x fewer atomic adds.
+// atomics instead, num_heads x 576 per (token, 64 rows). With 8 heads and
+// dense causal rows that is ~8x fewer atomic adds.
 //
 // A prepass per token builds the occupancy masks (bit r % 32 of word r / 32:
 // row r named), D = dO . O per head, and zeroes the token's dq. A token whose
@@ -399,36 +399,44 @@ sparse_mla_bwd_prep_kernel(const BwdArgs a, const KvMajorArgs m) {
   for (int w = tid; w < m.num_words; w += 256) m.mask[(int64_t)w * a.num_tokens + token] = dup ? 0u : s_bm[w];
 }
 
-// One workgroup = (kv block b, token chunk c); blockIdx.x = c * num_words + b.
-// Sized for two workgroups per CU (<= 80 KB of LDS, <= 256 registers per
-// lane), so that one workgroup's atomic and load waits overlap the other's
-// products.
-__global__ void __launch_bounds__(256, 2)
+// One workgroup = (two kv blocks bp = rows 64bp .. 64bp+63, token chunk c);
+// blockIdx.x = c * ceil(num_words / 2) + bp. A token's dq collects both
+// blocks before it is added. One workgroup per CU (155 KB of LDS), so the
+// compiler may use the whole register file to keep operand reads in flight.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
   constexpr int HB = 16;
-  __shared__ __attribute__((aligned(16))) uint8_t s_stage[kBwStage];        // the block's 32 rows
-  __shared__ __attribute__((aligned(16))) uint8_t s_q[1][HB * kBwPitch];    // the step's Q columns
-  __shared__ __attribute__((aligned(16))) uint8_t s_do[1][HB * kBwOPitch];  // the step's dO columns
-  __shared__ __attribute__((aligned(16))) float4_t s_dp[2][64];
-  __shared__ __attribute__((aligned(16))) uint8_t s_pt[HB * 64];
-  __shared__ __attribute__((aligned(16))) uint8_t s_dst[HB * 64];
-  __shared__ float s_D[1][HB], s_lse2[1][HB];
+  constexpr int KR = 2 * kTileKeys;   // kv rows of the workgroup (64)
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[KR * kBwPitch];   // the two blocks' rows
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[2][HB * kBwPitch];    // the step's Q columns, double-buffered
+  __shared__ __attribute__((aligned(16))) uint8_t s_do[2][HB * kBwOPitch];  // the step's dO columns
+  __shared__ __attribute__((aligned(16))) float4_t s_dp[4][64];              // dP^T per 16-key block
+  __shared__ __attribute__((aligned(16))) uint8_t s_pt[HB * 2 * KR];          // P, bf16 [column][64 keys]
+  __shared__ __attribute__((aligned(16))) uint8_t s_dst[HB * 2 * KR];         // s*dS, bf16 [column][64 keys]
+  __shared__ float s_D[2][HB], s_lse2[2][HB];
   __shared__ int s_tok[kKvChunk];
-  __shared__ uint32_t s_msk[kKvChunk];
+  __shared__ uint64_t s_msk[kKvChunk];
   __shared__ int s_np;
+  constexpr int kKP = 2 * KR;   // bytes per column row of s_pt / s_dst
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int b = (int)(blockIdx.x % m.num_words);
-  const int64_t t0 = (int64_t)(blockIdx.x / m.num_words) * kKvChunk;
-  const int64_t r0 = (int64_t)b * kTileKeys;
+  const int nbp = (m.num_words + 1) / 2;
+  const int bp = (int)(blockIdx.x % nbp);
+  const int64_t t0 = (int64_t)(blockIdx.x / nbp) * kKvChunk;
+  const int64_t r0 = (int64_t)bp * KR;
 
-  // the chunk's tokens that name rows of this block, in token order (the token list)
+  // the chunk's tokens that name rows of the two blocks, in token order (the
+  // token list), with a 64-bit mask of the named rows
   if (wave == 0) {
     const int64_t t = t0 + lane;
-    const uint32_t w = t < a.num_tokens ? m.mask[(int64_t)b * a.num_tokens + t] : 0u;
+    uint64_t w = 0;
+    if (t < a.num_tokens) {
+      w = m.mask[(int64_t)(2 * bp) * a.num_tokens + t];
+      if (2 * bp + 1 < m.num_words) w |= (uint64_t)m.mask[(int64_t)(2 * bp + 1) * a.num_tokens + t] << 32;
+    }
     const uint64_t act = __ballot(w != 0u);
     if (w != 0u) {
       const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(act >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)act, 0u));
@@ -455,9 +463,9 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
     return (ti < np && hh < a.num_heads) ? t0 + s_tok[ti] : (int64_t)-1;
   };
 
-  // the block's rows (rows past num_kv are 0; their mask bits are never set)
-#pragma unroll
-  for (int k = 0; k < kBwGran; ++k) {
+  // the blocks' rows (rows past num_kv are 0; their mask bits are never set)
+#pragma unroll 6
+  for (int k = 0; k < 2 * kBwGran; ++k) {
     const int gi = tid + 256 * k, row = gi / (kDqk / 8), c = gi % (kDqk / 8);
     bf16x8_t v = {};
     if (r0 + row < a.num_kv) v = *(const bf16x8_t*)(a.kv + (r0 + row) * a.kv_st + 8 * c);
@@ -518,75 +526,94 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
   store_step(0);
   __syncthreads();
 
-  // K (waves 0, 1) or V (waves 2, 3) rows of key block kb are the MFMA A
-  // operand, read from the block's rows: lane holds key kb*16 + n, columns 32c + 8g .. +7
+  // phase 1 roles: K (waves 0, 1) or V (waves 2, 3) of 16-key blocks
+  // kb = w & 1 and kb + 2 as the MFMA A operand (lane: key 16kb + n, columns 32c + 8g ..)
   const bool s_role = wave < 2;
   const int kb = wave & 1;
-  const uint8_t* arow = s_stage + (kb * 16 + n) * kBwPitch + 16 * g;
+  const uint8_t* arow0 = s_stage + (kb * 16 + n) * kBwPitch + 16 * g;
+  const uint8_t* arow1 = arow0 + 32 * kBwPitch;
 
-  // dkv of key block kb2 = w >> 1, column tiles 18(w & 1) .. +17: lane holds
-  // column 16dt + n of keys kb2*16 + 4g .. +3
+  // dkv of 16-key blocks kb2 = w >> 1 and kb2 + 2, column tiles 18(w & 1) .. +17:
+  // lane holds column 16dt + n of keys 16kb + 4g .. +3
   const int kb2 = wave >> 1;
-  float4_t dkv_acc[18];
+  float4_t dkv_acc[2][18];
 #pragma unroll
-  for (int k = 0; k < 18; ++k) dkv_acc[k] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int k = 0; k < 18; ++k) dkv_acc[j][k] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
   for (int p = 0; p < nsteps; ++p) {
-    const int buf = 0;
+    const int buf = p & 1;
     if (p + 1 < nsteps) load_step(p + 1);   // in flight during the three phases
     const uint8_t* sq = s_q[buf];
     const uint8_t* sd = s_do[buf];
 
-    // ---- phase 1: S^T (waves 0, 1) or dP^T (waves 2, 3) of key block kb, 16 heads
-    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- phase 1: S^T (waves 0, 1) or dP^T (waves 2, 3) of key blocks kb, kb + 2
+    float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
     if (s_role) {
 #pragma unroll
-      for (int c = 0; c < kDqk / 32; ++c)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow + 64 * c), lds16(sq + n * kBwPitch + 64 * c + 16 * g), acc, 0, 0, 0);
+      for (int c = 0; c < kDqk / 32; ++c) {
+        const bf16x8_t bv = lds16(sq + n * kBwPitch + 64 * c + 16 * g);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow0 + 64 * c), bv, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow1 + 64 * c), bv, acc1, 0, 0, 0);
+      }
     } else {
 #pragma unroll
-      for (int c = 0; c < kDv / 32; ++c)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow + 64 * c), lds16(sd + n * kBwOPitch + 64 * c + 16 * g), acc, 0, 0, 0);
-      s_dp[kb][lane] = acc;
+      for (int c = 0; c < kDv / 32; ++c) {
+        const bf16x8_t bv = lds16(sd + n * kBwOPitch + 64 * c + 16 * g);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow0 + 64 * c), bv, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow1 + 64 * c), bv, acc1, 0, 0, 0);
+      }
+      s_dp[kb][lane] = acc0;
+      s_dp[kb + 2][lane] = acc1;
     }
     __syncthreads();
 
-    // ---- phase 2: P and s*dS (lane: head n, keys kb*16 + 4g + e), masked by each column's token's rows
+    // ---- phase 2: P and s*dS (lane: column n, keys 16kb' + 4g + e), masked by each column's token's rows
     if (s_role) {
       const int ti = p * tpp + (n >> lhp);   // the token entry of this lane's column
-      const uint32_t msk = ti < np ? s_msk[ti] : 0u;
-      const float4_t dp = s_dp[kb][lane];
+      const uint64_t msk = ti < np ? s_msk[ti] : 0u;
       const float Dh = s_D[buf][n], l2 = s_lse2[buf][n];
-      float pv[4], ds[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ok = (msk >> (kb * 16 + 4 * g + e)) & 1u;
-        pv[e] = ok ? __builtin_amdgcn_exp2f(acc[e] * a.scale_log2 - l2) : 0.f;
-        ds[e] = pv[e] * (dp[e] - Dh) * a.scale;
+      for (int j = 0; j < 2; ++j) {
+        const int kbj = kb + 2 * j;
+        const float4_t sc = j ? acc1 : acc0;
+        const float4_t dp = s_dp[kbj][lane];
+        float pv[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = (msk >> (kbj * 16 + 4 * g + e)) & 1u;
+          pv[e] = ok ? __builtin_amdgcn_exp2f(sc[e] * a.scale_log2 - l2) : 0.f;
+          ds[e] = pv[e] * (dp[e] - Dh) * a.scale;
+        }
+        const int off = n * kKP + 2 * (kbj * 16 + 4 * g);
+        *(uint2*)(s_pt + off) = (uint2){pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+        *(uint2*)(s_dst + off) = (uint2){pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
       }
-      const int off = n * 64 + 2 * (kb * 16 + 4 * g);
-      *(uint2*)(s_pt + off) = (uint2){pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-      *(uint2*)(s_dst + off) = (uint2){pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
     }
     __syncthreads();
 
-    // ---- phase 3a: dq tiles 9w .. 9w+8 of the step's tokens += (s dS) K, added
-    // with atomics. All operand reads are issued before the first product.
+    // ---- phase 3a: dq tiles 9w .. 9w+8 of the step's tokens += (s dS) K over
+    // the 64 keys, added with atomics. Operand reads go ahead of the products.
     {
       const uint8_t* kt = s_stage + (8 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
-      const bf16x8_t ads = lds16(s_dst + n * 64 + 16 * g);
+      const bf16x8_t ads0 = lds16(s_dst + n * kKP + 16 * g);        // keys 8g ..
+      const bf16x8_t ads1 = lds16(s_dst + n * kKP + 64 + 16 * g);   // keys 32 + 8g ..
       float4_t c[9];
 #pragma unroll
       for (int k3 = 0; k3 < 9; k3 += 3) {
-        bf16x8_t bk[3];
+        bf16x8_t bk0[3], bk1[3];
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
           const int d0 = 16 * (9 * wave + k3 + k);
-          bk[k] = join4(lds_read_tr16(kt + 2 * d0), lds_read_tr16(kt + 4 * kBwPitch + 2 * d0));
+          bk0[k] = join4(lds_read_tr16(kt + 2 * d0), lds_read_tr16(kt + 4 * kBwPitch + 2 * d0));
+          bk1[k] = join4(lds_read_tr16(kt + 32 * kBwPitch + 2 * d0), lds_read_tr16(kt + 36 * kBwPitch + 2 * d0));
         }
 #pragma unroll
-        for (int k = 0; k < 3; ++k)
-          c[k3 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads, bk[k], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        for (int k = 0; k < 3; ++k) {
+          c[k3 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads0, bk0[k], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          c[k3 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads1, bk1[k], c[k3 + k], 0, 0, 0);
+        }
       }
       // row 4g + e of the tile is column 4g + e of the step; empty columns add nothing
 #pragma unroll
@@ -600,49 +627,55 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
         }
       }
     }
-    // ---- phase 3b: dkv of the block += (s dS)^T Q + P^T dO over the 16 heads (registers),
-    // operands read in two halves of 9 column tiles ahead of their products
+    // ---- phase 3b: dkv of key blocks kb2, kb2 + 2 += (s dS)^T Q + P^T dO over
+    // the 16 columns (registers); the Q and dO operands serve both key blocks
     {
-      const int aoff = (4 * g + (n >> 2)) * 64 + 2 * (kb2 * 16 + 4 * (n & 3));
-      const short4_t ads = lds_read_tr16(s_dst + aoff);
-      const short4_t ap = lds_read_tr16(s_pt + aoff);
+      short4_t ads[2], ap[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int aoff = (4 * g + (n >> 2)) * kKP + 2 * ((kb2 + 2 * j) * 16 + 4 * (n & 3));
+        ads[j] = lds_read_tr16(s_dst + aoff);
+        ap[j] = lds_read_tr16(s_pt + aoff);
+      }
       const uint8_t* bq = sq + (4 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
       const uint8_t* bo = sd + (4 * g + (n >> 2)) * kBwOPitch + 8 * (n & 3);
 #pragma unroll
-      for (int half = 0; half < 3; ++half) {
+      for (int part = 0; part < 3; ++part) {
         short4_t oq[6], oo[6];
 #pragma unroll
         for (int k = 0; k < 6; ++k) {
-          const int d0 = 16 * (18 * (wave & 1) + 6 * half + k);
+          const int d0 = 16 * (18 * (wave & 1) + 6 * part + k);
           oq[k] = lds_read_tr16(bq + 2 * d0);
           oo[k] = d0 < kDv ? lds_read_tr16(bo + 2 * d0) : (short4_t){};
         }
 #pragma unroll
         for (int k = 0; k < 6; ++k) {
-          const int d0 = 16 * (18 * (wave & 1) + 6 * half + k);
-          float4_t& acc2 = dkv_acc[6 * half + k];
-          acc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ads, oq[k], acc2, 0, 0, 0);
-          if (d0 < kDv) acc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap, oo[k], acc2, 0, 0, 0);
+          const int d0 = 16 * (18 * (wave & 1) + 6 * part + k);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float4_t& acc2 = dkv_acc[j][6 * part + k];
+            acc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ads[j], oq[k], acc2, 0, 0, 0);
+            if (d0 < kDv) acc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap[j], oo[k], acc2, 0, 0, 0);
+          }
         }
       }
     }
-    __syncthreads();   // every wave is done with this step's Q, dO, P and s*dS
-    if (p + 1 < nsteps) {
-      store_step(0);
-      __syncthreads();
-    }
+    if (p + 1 < nsteps) store_step(buf ^ 1);   // the other buffer: last read before the previous step's barrier
+    __syncthreads();
   }
 
-  // ---- the block's dkv, once per workgroup (other chunks add to the same rows)
+  // ---- the blocks' dkv, once per workgroup (other chunks add to the same rows)
 #pragma unroll
-  for (int k = 0; k < 18; ++k) {
-    const int d0 = 16 * (18 * (wave & 1) + k);
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t r = r0 + kb2 * 16 + 4 * g + e;
-      if (r < a.num_kv) unsafeAtomicAdd(a.dkv + r * a.dkv_st + d0 + n, dkv_acc[k][e]);
+    for (int k = 0; k < 18; ++k) {
+      const int d0 = 16 * (18 * (wave & 1) + k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t r = r0 + (kb2 + 2 * j) * 16 + 4 * g + e;
+        if (r < a.num_kv) unsafeAtomicAdd(a.dkv + r * a.dkv_st + d0 + n, dkv_acc[j][k][e]);
+      }
     }
-  }
 }
 
 // dkv = 0 before the backward accumulates into it: one thread per float4.

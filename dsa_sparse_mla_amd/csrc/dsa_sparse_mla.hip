@@ -438,7 +438,8 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
                                       round_up(num_tokens * 4, 256));
     m.num_words = (int32_t)words;
     hipLaunchKernelGGL(dsa::sparse_mla_bwd_prep_kernel, dim3((unsigned)num_tokens), dim3(256), 0, s, a, m);
-    hipLaunchKernelGGL(dsa::sparse_mla_bwd_kv_kernel, dim3((unsigned)(words * chunks)), dim3(256), 0, s, a, m);
+    hipLaunchKernelGGL(dsa::sparse_mla_bwd_kv_kernel, dim3((unsigned)((words + 1) / 2 * chunks)), dim3(256), 0, s, a,
+                       m);
     a.only = m.dup;   // rows with a repeated entry: token-major
     hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, s, a);
     const bool launched = hipGetLastError() == hipSuccess;

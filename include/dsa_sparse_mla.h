@@ -186,7 +186,7 @@ int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stri
  * token and head block adds each named row's gradient into dkv. kv-major,
  * when num_heads <= 16, 0 < num_kv <= 262144 and 3 * num_kv * num_heads <=
  * 64 * topk (rows that name a large share of kv, as in causal prefill): one
- * workgroup per (32-row kv block, 64-token chunk) keeps the block's dkv in
+ * workgroup per (64 kv rows, 64-token chunk) keeps the rows' dkv in
  * registers and adds dq with atomics instead, so dq too may then differ in
  * the last bits between calls. Tokens whose row names some kv row twice go
  * to the token-major kernel within the same call. The kv-major schedule takes
