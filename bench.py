@@ -11,9 +11,9 @@ sparse MLA backend", Performance > Isolated sparse MLA forward).
 With --op bwd it times the backward instead (flat workloads): one step is
 one backward call (the dkv zero fill, then the token-major kernel, or the
 kv-major prepass and pass with the token-major kernel for rows that repeat
-an entry), after one forward that supplies out and LSE; `value` then counts 3456 bytes per valid key (the 1152-byte
-gathered row and its 2304-byte fp32 dkv addition) and `tflops` 5504 flops
-per valid key and head.
+an entry), after one forward that supplies out and LSE; `value` then counts
+the 1152-byte gathered row per valid key, as for the forward, and `tflops`
+5504 flops per valid key and head.
 
 Prints one JSON line. `value` is the gathered-KV bandwidth (1152 bytes per
 valid key: one 576-wide bf16 row, shared by every head) over the average step
@@ -41,9 +41,12 @@ METRIC = "sparse MLA fwd TFLOP/s + gathered-KV GB/s (% roofline), topk=2048, dqk
 ROW_BYTES = 576 * 2
 FLOP_PER_KEY_HEAD = 2 * (576 + 512)
 # backward: QK^T (576), dO V^T (512), dQ (576), dK (576), dV (512) per key and head
-BWD_METRIC = "sparse MLA bwd TFLOP/s + gathered-KV/dKV GB/s (% roofline), topk=2048, dqk576/dv512"
+BWD_METRIC = "sparse MLA bwd TFLOP/s + gathered-KV GB/s (% roofline), topk=2048, dqk576/dv512"
 BWD_FLOP_PER_KEY_HEAD = 2 * (3 * 576 + 2 * 512)
-BWD_BYTES_PER_KEY = ROW_BYTES + 576 * 4   # the gathered row, and its fp32 dkv addition
+# the gathered row, as for the forward: the fp32 gradient row each key
+# receives is summed in registers by the kv-major schedule, so it is not
+# counted as moved bytes (the counters give what the token-major one moves)
+BWD_BYTES_PER_KEY = ROW_BYTES
 
 
 def source_hash() -> str:

@@ -83,5 +83,5 @@ def test_flop_and_byte_constants():
     assert bench.FLOP_PER_KEY_HEAD == 2 * (576 + 512)
     assert bench.ROW_BYTES == 1152
     assert bench.BWD_FLOP_PER_KEY_HEAD == 2 * (3 * 576 + 2 * 512)
-    assert bench.BWD_BYTES_PER_KEY == 1152 + 576 * 4
+    assert bench.BWD_BYTES_PER_KEY == 1152
     assert np.isclose(bench.HBM_PEAK_GBPS, 8000.0) and np.isclose(bench.MFMA_BF16_PEAK_TFLOPS, 2500.0)
