@@ -260,3 +260,30 @@ def test_bwd_paths_of_the_cases():
     d = workloads.make_flat("swe")
     assert kv_major(d["q"].shape[1], d["kv"].shape[0], d["indices"].shape[1])
     assert not kv_major(64, 300, 100)
+
+
+@pytest.mark.parametrize("N", [262144, 262145])
+def test_bwd_kv_major_size_limit(N):
+    """The kv-major schedule's limits: 262144 kv rows (8192 mask words, the
+    prepass's whole LDS bitmap) with 3 N H = 64 topk exactly takes it; one row
+    more takes the token-major kernel. Both against the oracle."""
+    T, H, topk = 3, 1, 12288
+    assert kv_major(H, N, topk) == (N == 262144)
+    rng = np.random.default_rng(N)
+    g = torch.Generator().manual_seed(N)
+    q = torch.randn((T, H, 576), generator=g).to(torch.bfloat16)
+    kv = torch.randn((N, 576), generator=g).to(torch.bfloat16)
+    dout = torch.randn((T, H, 512), generator=g).to(torch.bfloat16)
+    planted = np.array([0, N - 1, N - 2, 31, 32])   # first and last rows, a block edge
+    rows = [np.concatenate([planted, rng.choice(np.setdiff1d(np.arange(N), planted), topk - 5, replace=False)])]
+    rows += [rng.choice(N, topk, replace=False) for _ in range(T - 1)]
+    idx = torch.from_numpy(np.stack(rows).astype(np.int32))
+    dq, dkv = run(q, kv, idx, 1 / 24, dout)
+    rdq, rdkv = ref(q, kv, idx, 1 / 24, dout)
+    check_grad(np64(dq), rdq, f"dq N={N}")
+    named = np.unique(idx.numpy())
+    named_t = torch.from_numpy(named).long().to(dkv.device)
+    check_grad(np64(dkv[named_t]), rdkv[named], f"dkv N={N} (named rows)")
+    unnamed = torch.ones(N, dtype=torch.bool, device=dkv.device)
+    unnamed[named_t] = False
+    assert bool((dkv[unnamed] == 0).all())
