@@ -472,48 +472,64 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
     *(bf16x8_t*)(s_stage + row * kBwPitch + 16 * c) = v;
   }
 
+  // the arguments the step loop uses, as values: the lambdas below capture by
+  // reference, and through a reference to the argument block the compiler
+  // re-read them from memory in every step
+  const uint16_t* const q_ptr = a.q;
+  const uint16_t* const do_ptr = a.dout;
+  const float* const lse_ptr = a.lse;
+  const float* const dbuf = m.dbuf;
+  float* const dq_ptr = a.dq;
+  const int64_t q_st = a.q_st, q_sh = a.q_sh, do_st = a.do_st, do_sh = a.do_sh, lse_st = a.lse_st;
+  const int64_t dq_st = a.dq_st, dq_sh = a.dq_sh;
+  const int num_heads = a.num_heads;
+  const float scale = a.scale, scale_log2 = a.scale_log2;
+
   // Q (16 columns x 72 granules) and dO (16 x 64) of step p: thread tid holds granules tid + 256k
   constexpr int kPairGran = (HB * (kDqk / 8) + HB * (kDv / 8) + 255) / 256;   // 9
   bf16x8_t preg[kPairGran];
+  uint32_t pvalid = 0;   // bit k: granule k holds data (else it is stored as 0)
   float pl2 = 0.f, pD = 0.f;
   bool pok = false;
+  // Branch-free: every granule's load is issued, those of empty columns from
+  // q's first element, and zeroed when stored. Conditional loads here had
+  // split the issue into branches with waits between them.
   auto load_step = [&](int p) {
+    pvalid = 0;
 #pragma unroll
     for (int k = 0; k < kPairGran; ++k) {
       const int gi = tid + 256 * k;
-      bf16x8_t v = {};
-      int hh;
-      if (gi < HB * (kDqk / 8)) {
-        const int h = gi / (kDqk / 8), c = gi % (kDqk / 8);
-        const int64_t t = column(p, h, hh);
-        if (t >= 0) v = *(const bf16x8_t*)(a.q + t * a.q_st + (int64_t)hh * a.q_sh + 8 * c);
-      } else if (gi < HB * (kDqk / 8) + HB * (kDv / 8)) {
-        const int gj = gi - HB * (kDqk / 8), h = gj / (kDv / 8), c = gj % (kDv / 8);
-        const int64_t t = column(p, h, hh);
-        if (t >= 0) v = *(const bf16x8_t*)(a.dout + t * a.do_st + (int64_t)hh * a.do_sh + 8 * c);
-      }
-      preg[k] = v;
+      const bool isq = gi < HB * (kDqk / 8);
+      const int gj = isq ? gi : gi - HB * (kDqk / 8);
+      const int h = isq ? gj / (kDqk / 8) : gj / (kDv / 8);
+      const int c = isq ? gj % (kDqk / 8) : gj % (kDv / 8);
+      const int ti = p * tpp + (h >> lhp), hh = h & (hp - 1);
+      const bool ok = gi < HB * (kDqk / 8) + HB * (kDv / 8) && ti < np && hh < num_heads;
+      const int64_t t = t0 + s_tok[ti < np ? ti : np - 1];
+      const uint16_t* src = isq ? q_ptr + t * q_st + hh * q_sh + 8 * c : do_ptr + t * do_st + hh * do_sh + 8 * c;
+      preg[k] = *(const bf16x8_t*)(ok ? src : q_ptr);
+      pvalid |= (uint32_t)ok << k;
     }
-    if (tid < HB) {
-      int hh;
-      const int64_t t = column(p, tid, hh);
-      pok = t >= 0;
-      if (pok) {
-        pl2 = a.lse[t * a.lse_st + hh];   // scaled when stored: no wait on the loads here
-        pD = m.dbuf[t * 16 + hh];
-      }
+    {
+      const int h = tid & (HB - 1);
+      const int ti = p * tpp + (h >> lhp), hh = h & (hp - 1);
+      pok = ti < np && hh < num_heads;
+      const int64_t t = t0 + s_tok[ti < np ? ti : np - 1];
+      pl2 = *(pok ? lse_ptr + t * lse_st + hh : lse_ptr);   // scaled when stored: no wait on the loads here
+      pD = *(pok ? dbuf + t * 16 + hh : dbuf);
     }
   };
   auto store_step = [&](int buf) {
 #pragma unroll
     for (int k = 0; k < kPairGran; ++k) {
       const int gi = tid + 256 * k;
+      const bf16x8_t v = (pvalid >> k) & 1u ? preg[k] : (bf16x8_t){};
       if (gi < HB * (kDqk / 8)) {
         const int h = gi / (kDqk / 8), c = gi % (kDqk / 8);
-        *(bf16x8_t*)(s_q[buf] + h * kBwPitch + 16 * c) = preg[k];
+        *(bf16x8_t*)(s_q[buf] + h * kBwPitch + 16 * c) = v;
       } else if (gi < HB * (kDqk / 8) + HB * (kDv / 8)) {
         const int gj = gi - HB * (kDqk / 8), h = gj / (kDv / 8), c = gj % (kDv / 8);
-        *(bf16x8_t*)(s_do[buf] + h * kBwOPitch + 16 * c) = preg[k];
+        *(bf16x8_t*)(s_do[buf] + h * kBwOPitch + 16 * c) = v;
       }
     }
     if (tid < HB) {
@@ -583,8 +599,8 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool ok = (msk >> (kbj * 16 + 4 * g + e)) & 1u;
-          pv[e] = ok ? __builtin_amdgcn_exp2f(sc[e] * a.scale_log2 - l2) : 0.f;
-          ds[e] = pv[e] * (dp[e] - Dh) * a.scale;
+          pv[e] = ok ? __builtin_amdgcn_exp2f(sc[e] * scale_log2 - l2) : 0.f;
+          ds[e] = pv[e] * (dp[e] - Dh) * scale;
         }
         const int off = n * kKP + 2 * (kbj * 16 + 4 * g);
         *(uint2*)(s_pt + off) = (uint2){pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
@@ -621,7 +637,7 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
         int hh;
         const int64_t t = column(p, 4 * g + e, hh);
         if (t >= 0) {
-          float* dqt = a.dq + t * a.dq_st + (int64_t)hh * a.dq_sh + n;
+          float* dqt = dq_ptr + t * dq_st + hh * dq_sh + n;
 #pragma unroll
           for (int k = 0; k < 9; ++k) unsafeAtomicAdd(dqt + 16 * (9 * wave + k), c[k][e]);
         }
