@@ -11,10 +11,12 @@
 //   dkv[J,:512] += P^T dO             (the value use)
 // Entries that name no row get nothing; duplicates count once per occurrence.
 //
-// One workgroup of 4 waves handles one token and a block of 16 heads (32 when
-// the call has more than 16 heads: see the kernel's HT). The
-// index row is compacted per 2048-entry segment, as in the forward. Per tile
-// of 32 keys:
+// Two schedules. The token-major kernel (below): one workgroup of 4 waves
+// handles one token and a block of 16 heads (32 when the call has more than
+// 16 heads: see the kernel's HT). The kv-major pass (further below) serves
+// up to 16 heads when index rows name a large share of the kv rows. In the
+// token-major kernel the index row is compacted per 2048-entry segment, as in
+// the forward. Per tile of 32 keys:
 //   phase 1: waves 0,1: S^T = K Q^T on key block 0 / 1 (16x16x32 MFMA, Q^T
 //            in registers); waves 2,3: dP^T = V dO^T likewise (dO^T in
 //            registers), handed to waves 0,1 through LDS;
@@ -548,6 +550,11 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
   const int kb = wave & 1;
   const uint8_t* arow0 = s_stage + (kb * 16 + n) * kBwPitch + 16 * g;
   const uint8_t* arow1 = arow0 + 32 * kBwPitch;
+  // key block kb's operand stays in registers for the whole chunk (the rows
+  // do not change); kb + 2's is read from LDS in each step
+  bf16x8_t areg[kDqk / 32];
+#pragma unroll
+  for (int c = 0; c < kDqk / 32; ++c) areg[c] = (s_role || c < kDv / 32) ? lds16(arow0 + 64 * c) : (bf16x8_t){};
 
   // dkv of 16-key blocks kb2 = w >> 1 and kb2 + 2, column tiles 18(w & 1) .. +17:
   // lane holds column 16dt + n of keys 16kb + 4g .. +3
@@ -570,14 +577,14 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
 #pragma unroll
       for (int c = 0; c < kDqk / 32; ++c) {
         const bf16x8_t bv = lds16(sq + n * kBwPitch + 64 * c + 16 * g);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow0 + 64 * c), bv, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(areg[c], bv, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow1 + 64 * c), bv, acc1, 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int c = 0; c < kDv / 32; ++c) {
         const bf16x8_t bv = lds16(sd + n * kBwOPitch + 64 * c + 16 * g);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow0 + 64 * c), bv, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(areg[c], bv, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(arow1 + 64 * c), bv, acc1, 0, 0, 0);
       }
       s_dp[kb][lane] = acc0;
