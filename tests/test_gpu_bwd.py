@@ -287,3 +287,36 @@ def test_bwd_kv_major_size_limit(N):
     unnamed = torch.ones(N, dtype=torch.bool, device=dkv.device)
     unnamed[named_t] = False
     assert bool((dkv[unnamed] == 0).all())
+
+
+def test_bwd_kv_major_strided():
+    """The kv-major schedule on strided views: q every other head of a wider
+    tensor, kv rows 640 apart, index rows with trailing columns, dO a head
+    slice, dq and dkv views into larger buffers that must stay untouched
+    outside the views."""
+    T, H, N, k = 100, 8, 150, 120
+    assert kv_major(H, N, k)
+    q_big, kv, idx, dout_big = random_case(T, 2 * H, N, k, seed=31, dup=False)
+    q = q_big[:, ::2]
+    dout = dout_big[:, 3:3 + H]
+    kv_big = torch.zeros((N, 640), dtype=torch.bfloat16)
+    kv_big[:, :576] = kv
+    idx_big = torch.full((T, k + 8), 7, dtype=torch.int32)
+    idx_big[:, :k] = idx
+    dsa = _dsa()
+    qd = q_big.to(DEV)[:, ::2]
+    dod = dout_big.to(DEV)[:, 3:3 + H]
+    kvd = kv_big.to(DEV)[:, :576]
+    idd = idx_big.to(DEV)[:, :k]
+    o, l = sparse_mla_fwd_ref(np64(q), np64(kv), idx.numpy(), 1 / 24)
+    out = torch.from_numpy(o).to(torch.bfloat16).to(DEV)
+    lse = torch.from_numpy(l).float().to(DEV)
+    dq_big = torch.full((T, H, 640), 7.0, device=DEV)
+    dkv_big = torch.full((N, 600), 7.0, device=DEV)
+    dq, dkv = dsa.sparse_mla_bwd(qd, kvd, idd, 1 / 24, out, lse, dod,
+                                 dq=dq_big[:, :, :576], dkv=dkv_big[:, :576])
+    torch.cuda.synchronize()
+    assert (dq_big[:, :, 576:] == 7.0).all() and (dkv_big[:, 576:] == 7.0).all()
+    rdq, rdkv = ref(q, kv, idx, 1 / 24, dout)
+    check_grad(np64(dq), rdq, "dq strided kv-major")
+    check_grad(np64(dkv), rdkv, "dkv strided kv-major")
