@@ -185,7 +185,7 @@ int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stri
  * Two schedules, chosen from the sizes alone. Token-major: one workgroup per
  * token and head block adds each named row's gradient into dkv. kv-major,
  * when num_heads <= 16, 0 < num_kv <= 262144 and 3 * num_kv * num_heads <=
- * 64 * topk (rows that name a large share of kv, as in causal prefill): one
+ * 256 * topk (rows that name a large share of kv, as in causal prefill): one
  * workgroup per (64 kv rows, 64-token chunk) keeps the rows' dkv in
  * registers and adds dq with atomics instead, so dq too may then differ in
  * the last bits between calls. Tokens whose row names some kv row twice go

@@ -80,8 +80,8 @@ def run(q, kv, idx, sm, dout, own_forward=False):
 def kv_major(H, N, topk):
     """The library's choice of the kv-major pass (stated with the backward in
     include/dsa_sparse_mla.h): at most 16 heads, at most 262144 kv rows, and
-    topk at least 3/64 of H x num_kv."""
-    return H <= 16 and 0 < N <= 32 * 8192 and 3 * N * H <= 64 * topk
+    topk at least 3/256 of H x num_kv."""
+    return H <= 16 and 0 < N <= 32 * 8192 and 3 * N * H <= 256 * topk
 
 
 def ref(q, kv, idx, sm, dout):
@@ -254,9 +254,11 @@ def test_bwd_kv_major_causal_rows():
 
 
 def test_bwd_paths_of_the_cases():
-    """The cases above reach both kernels: the token-major one at 8+ heads
-    with sparse rows, the kv-major pass for the SWE-like rows."""
-    assert not kv_major(8, 300, 100) and kv_major(1, 300, 100)
+    """The cases above reach both kernels: the token-major one above 16 heads
+    and for sparse rows (5000 kv rows, topk up to 64, 8 heads), the kv-major
+    pass for the SWE-like rows and the small dense cases."""
+    assert not kv_major(8, 5000, 64) and not kv_major(8, 5000, 1) and kv_major(8, 5000, 2049)
+    assert kv_major(8, 300, 100) and kv_major(16, 300, 100) and not kv_major(17, 300, 100)
     d = workloads.make_flat("swe")
     assert kv_major(d["q"].shape[1], d["kv"].shape[0], d["indices"].shape[1])
     assert not kv_major(64, 300, 100)
@@ -265,9 +267,9 @@ def test_bwd_paths_of_the_cases():
 @pytest.mark.parametrize("N", [262144, 262145])
 def test_bwd_kv_major_size_limit(N):
     """The kv-major schedule's limits: 262144 kv rows (8192 mask words, the
-    prepass's whole LDS bitmap) with 3 N H = 64 topk exactly takes it; one row
-    more takes the token-major kernel. Both against the oracle."""
-    T, H, topk = 3, 1, 12288
+    prepass's whole LDS bitmap) with 3 N H = 256 topk exactly takes it; one
+    row more takes the token-major kernel. Both against the oracle."""
+    T, H, topk = 3, 1, 3072
     assert kv_major(H, N, topk) == (N == 262144)
     rng = np.random.default_rng(N)
     g = torch.Generator().manual_seed(N)
@@ -320,3 +322,19 @@ def test_bwd_kv_major_strided():
     rdq, rdkv = ref(q, kv, idx, 1 / 24, dout)
     check_grad(np64(dq), rdq, "dq strided kv-major")
     check_grad(np64(dkv), rdkv, "dkv strided kv-major")
+
+
+def test_bwd_kv_major_long_causal_rows():
+    """Causal rows longer than topk (token t names 256 of its t + 1 keys once
+    t > 255, tail padding before that): sparser blocks than the dense causal
+    case, still on the kv-major schedule at 8 heads."""
+    d = workloads.make_flat("wide", num_tokens=600, num_heads=8, topk=256)
+    T, H = d["q"].shape[:2]
+    N = d["kv"].shape[0]
+    assert kv_major(H, N, 256)
+    g = torch.Generator().manual_seed(13)
+    dout = torch.randn((T, H, 512), generator=g).to(torch.bfloat16)
+    dq, dkv = run(d["q"], d["kv"], d["indices"], d["sm_scale"], dout)
+    rdq, rdkv = ref(d["q"], d["kv"], d["indices"], d["sm_scale"], dout)
+    check_grad(np64(dq), rdq, "dq long causal kv-major")
+    check_grad(np64(dkv), rdkv, "dkv long causal kv-major")
