@@ -312,10 +312,12 @@ def main():
         dsa.sparse_mla_fwd(d["q"], d["kv"], d["indices"], d["sm_scale"], out=out, lse=lse, workspace=ws)
         dq = torch.empty((T, H, 576), dtype=torch.float32, device=dev)
         dkv = torch.empty((d["kv"].shape[0], 576), dtype=torch.float32, device=dev)
+        bwd_schedule, bwd_ws_bytes = dsa.bwd_workspace_size(T, H, d["kv"].shape[0], d["indices"].shape[1])
+        bwd_ws = torch.empty(max(bwd_ws_bytes, 256), dtype=torch.uint8, device=dev)
 
         def step():
             dsa.sparse_mla_bwd(d["q"], d["kv"], d["indices"], d["sm_scale"], out, lse, dout,
-                               dq=dq, dkv=dkv)
+                               dq=dq, dkv=dkv, workspace=bwd_ws)
     elif "kv" in d:
         def step():
             dsa.sparse_mla_fwd(d["q"], d["kv"], d["indices"], d["sm_scale"], out=out, lse=lse,
@@ -416,6 +418,7 @@ def main():
     }
     if args.op == "bwd":
         rec["config"]["op"] = "bwd"
+        rec["config"]["schedule"] = bwd_schedule
         rec["bytes_per_key"] = BWD_BYTES_PER_KEY
     if args.cpu_budget > 0:
         if args.op == "bwd":

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     DQK,
     DV,
     LIB_PATH,
+    bwd_workspace_size,
     DsaError,
     lib,
     sparse_mla_bwd,
@@ -21,4 +22,4 @@ from .binding import (  # noqa: F401
     workspace_size,
 )
 
-__all__ = ["sparse_mla_fwd", "sparse_mla_fwd_paged", "sparse_mla_bwd", "workspace_size", "DsaError", "lib"]
+__all__ = ["sparse_mla_fwd", "sparse_mla_fwd_paged", "sparse_mla_bwd", "workspace_size", "bwd_workspace_size", "DsaError", "lib"]

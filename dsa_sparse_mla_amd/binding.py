@@ -77,7 +77,11 @@ def lib() -> ctypes.CDLL:
             vp, i64, i64,            # dout
             vp, i64, i64,            # dq
             vp, i64,                 # dkv, row stride
+            vp, i64,                 # workspace, bytes
             vp]                      # stream
+        L.dsa_sparse_mla_bwd_workspace_size.restype = ctypes.c_int
+        L.dsa_sparse_mla_bwd_workspace_size.argtypes = [i64, i32, i64, i32,
+                                                        ctypes.POINTER(i32), ctypes.POINTER(i64)]
         L.dsa_sparse_mla_workspace_size.restype = ctypes.c_int
         L.dsa_sparse_mla_workspace_size.argtypes = [i64, i32, i32, i32,
                                                     ctypes.POINTER(i32), ctypes.POINTER(i64)]
@@ -100,6 +104,20 @@ def workspace_size(num_tokens: int, num_heads: int, topk: int, num_splits: int =
     if st != 0:
         raise DsaError(st, "dsa_sparse_mla_workspace_size")
     return s.value, b.value
+
+
+BWD_SCHEDULES = {0: "token-major", 1: "kv-major"}
+
+
+def bwd_workspace_size(num_tokens: int, num_heads: int, num_kv: int, topk: int):
+    """(schedule name, bytes) that a backward call with these sizes uses."""
+    s = ctypes.c_int32(0)
+    b = ctypes.c_int64(0)
+    st = lib().dsa_sparse_mla_bwd_workspace_size(num_tokens, num_heads, num_kv, topk,
+                                                 ctypes.byref(s), ctypes.byref(b))
+    if st != 0:
+        raise DsaError(st, "dsa_sparse_mla_bwd_workspace_size")
+    return BWD_SCHEDULES[s.value], b.value
 
 
 def _check(t: torch.Tensor, name: str, dtype, ndim: int, device):
@@ -212,13 +230,15 @@ def sparse_mla_fwd_paged(q, kv_pages, page_table, seq_lens, indices, sm_scale, q
     return out, lse
 
 
-def sparse_mla_bwd(q, kv, indices, sm_scale, out, lse, dout, dq=None, dkv=None):
+def sparse_mla_bwd(q, kv, indices, sm_scale, out, lse, dout, dq=None, dkv=None, workspace=None):
     """Sparse MLA backward over flat KV: gradients of the forward output.
 
     q [T,H,576] bf16, kv [N,576] bf16, indices [T,topk] int32 as in the
     forward; out [T,H,512] bf16 and lse [T,H] fp32 from the forward on these
     inputs; dout [T,H,512] bf16. Returns (dq [T,H,576] fp32, dkv [N,576] fp32);
-    dkv is written in full (rows no index names are 0).
+    dkv is written in full (rows no index names are 0). The workspace (a
+    uint8 device tensor of at least bwd_workspace_size() bytes) is allocated
+    here with torch when the schedule needs one and none is given.
     """
     dev = q.device
     _check(q, "q", torch.bfloat16, 3, dev)
@@ -243,6 +263,12 @@ def sparse_mla_bwd(q, kv, indices, sm_scale, out, lse, dout, dq=None, dkv=None):
     _check(dkv, "dkv", torch.float32, 2, dev)
     if tuple(dq.shape) != (T, H, DQK) or tuple(dkv.shape) != (N, DQK):
         raise ValueError("dq must be [T, H, 576] and dkv [N, 576]")
+    _, need = bwd_workspace_size(T, H, N, indices.shape[1])
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib().dsa_sparse_mla_bwd(
@@ -255,6 +281,7 @@ def sparse_mla_bwd(q, kv, indices, sm_scale, out, lse, dout, dq=None, dkv=None):
             dout.data_ptr(), dout.stride(0), dout.stride(1),
             dq.data_ptr(), dq.stride(0), dq.stride(1),
             dkv.data_ptr(), dkv.stride(0),
+            ws_ptr, ws_bytes,
             stream)
     if st != 0:
         raise DsaError(st, "dsa_sparse_mla_bwd")

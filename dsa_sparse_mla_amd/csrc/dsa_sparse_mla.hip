@@ -147,6 +147,44 @@ int device_check() {
   return d->gfx950 ? DSA_OK : DSA_ERR_UNSUPPORTED;
 }
 
+// Backward schedule and workspace, from the sizes alone.
+//
+// kv-major when the rows are dense enough: per (token, 64 kv rows) it adds
+// H x 576 to dq where the token-major kernel adds 576 per named row, and its
+// steps carry every column. The shapes stand in for the density: topk at
+// least 3/256 of H x num_kv, i.e. uniform rows name 0.75 H or more of every
+// 64 rows. Measured: 2.9x faster on 8192-token causal rows at 8 heads, 1.5x
+// at 16, 4.7x on packed documents at 8 heads. Its workspace holds the
+// per-token occupancy masks ([word][token] u32), the per-token repeat flags
+// and D = dout . out per (token, head); above 1 GiB of it the token-major
+// kernel runs instead.
+struct BwdPlan {
+  int schedule = DSA_BWD_TOKEN_MAJOR;
+  int64_t words = 0, chunks = 0;
+  int64_t dup_off = 0, d_off = 0;
+  int64_t ws_bytes = 0;
+};
+
+void bwd_plan(int64_t T, int32_t H, int64_t N, int32_t topk, BwdPlan* p) {
+  *p = BwdPlan();
+  if (T <= 0 || N <= 0) return;
+  const int64_t words = (N + 31) / 32;
+  const int64_t chunks = (T + dsa::kKvChunk - 1) / dsa::kKvChunk;
+  const int64_t mask_bytes = words * T * 4;
+  const int64_t dup_off = round_up(mask_bytes, 256);
+  const int64_t d_off = dup_off + round_up(T * 4, 256);
+  const int64_t bytes = d_off + T * 16 * 4;
+  const bool kv_major = H <= 16 && words <= dsa::kKvMaxWords && 3 * N * H <= 256 * (int64_t)topk &&
+                        bytes <= ((int64_t)1 << 30) && words * chunks < ((int64_t)1 << 31);
+  if (!kv_major) return;
+  p->schedule = DSA_BWD_KV_MAJOR;
+  p->words = words;
+  p->chunks = chunks;
+  p->dup_off = dup_off;
+  p->d_off = d_off;
+  p->ws_bytes = bytes;
+}
+
 // Heads per workgroup: 16, 32 or 64 (HT head tiles of 16); more heads use
 // several workgroups per token, one per block of 64.
 template <bool PAGED>
@@ -341,7 +379,8 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
                        float sm_scale, const void* out, int64_t out_stride_tok, int64_t out_stride_head,
                        const float* lse, int64_t lse_stride_tok, const void* dout, int64_t dout_stride_tok,
                        int64_t dout_stride_head, float* dq, int64_t dq_stride_tok, int64_t dq_stride_head,
-                       float* dkv, int64_t dkv_stride_row, void* stream) {
+                       float* dkv, int64_t dkv_stride_row, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
   // q/out/lse checks are those of the forward (out and dout share its layout rules)
   int st = check_common(q, q_stride_tok, q_stride_head, indices, idx_stride_tok, num_tokens, num_heads, topk,
                         out, out_stride_tok, out_stride_head, lse, lse_stride_tok);
@@ -363,15 +402,23 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
     if (num_tokens > 1 && (dout_stride_tok == 0 || dq_stride_tok == 0)) return DSA_ERR_INVALID_ARGUMENT;
     if (num_heads > 1 && (dout_stride_head < DSA_DV || dq_stride_head < DSA_DQK)) return DSA_ERR_INVALID_ARGUMENT;
   }
+  if (workspace_bytes < 0) return DSA_ERR_INVALID_ARGUMENT;
+  BwdPlan plan;
+  bwd_plan(num_tokens, num_heads, num_kv, topk, &plan);
+  const int64_t ws_used = plan.ws_bytes;
   st = check_overlaps(
       {extent3(dq, num_tokens, dq_stride_tok, num_heads, dq_stride_head, DSA_DQK, 4),
-       extent2(dkv, num_kv, dkv_stride_row, DSA_DQK, 4)},
+       extent2(dkv, num_kv, dkv_stride_row, DSA_DQK, 4),
+       extent2(ws_used > 0 ? workspace : nullptr, 1, 0, ws_used, 1)},
       {extent3(q, num_tokens, q_stride_tok, num_heads, q_stride_head, DSA_DQK, 2),
        extent2(kv, num_kv, kv_stride_row, DSA_DQK, 2), extent2(indices, num_tokens, idx_stride_tok, topk, 4),
        extent3(out, num_tokens, out_stride_tok, num_heads, out_stride_head, DSA_DV, 2),
        extent2(lse, num_tokens, lse_stride_tok, num_heads, 4),
        extent3(dout, num_tokens, dout_stride_tok, num_heads, dout_stride_head, DSA_DV, 2)});
   if (st != DSA_OK) return st;
+  // checked before anything is enqueued: a call that fails launches nothing
+  if (ws_used > 0 && (!workspace || workspace_bytes < ws_used || !aligned(workspace, 256)))
+    return DSA_ERR_WORKSPACE;
   st = device_check();
   if (st != DSA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -417,42 +464,35 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
   const int64_t wgs = num_tokens * a.head_blocks;
   if (wgs >= ((int64_t)1 << 31)) return DSA_ERR_UNSUPPORTED;
 
-  // kv-major pass when the rows are dense enough: per (token, 64 kv rows) it
-  // adds H x 576 to dq where the token-major kernel adds 576 per named row,
-  // and its steps carry every column. The shapes stand in for the density:
-  // topk at least 3/256 of H x num_kv, i.e. uniform rows name 0.75 H or more
-  // of every 64 rows. Measured: 2.9x faster on 8192-token causal rows at 8
-  // heads, 1.5x at 16, 4.7x on packed documents at 8 heads.
-  const int64_t words = (num_kv + 31) / 32;
-  const int64_t chunks = (num_tokens + dsa::kKvChunk - 1) / dsa::kKvChunk;
-  const int64_t mask_bytes = words * num_tokens * 4;
-  const int64_t ws_bytes = round_up(mask_bytes, 256) + round_up(num_tokens * 4, 256) + num_tokens * 16 * 4;
-  const bool kv_major = num_heads <= 16 && num_kv > 0 && words <= dsa::kKvMaxWords &&
-                        3 * num_kv * num_heads <= 256 * (int64_t)topk && ws_bytes <= ((int64_t)1 << 30) &&
-                        words * chunks < ((int64_t)1 << 31);
-  void* ws = nullptr;
-  if (kv_major && hipMallocAsync(&ws, (size_t)ws_bytes, s) == hipSuccess && ws) {
+  if (plan.schedule == DSA_BWD_KV_MAJOR) {
     dsa::KvMajorArgs m;
-    m.mask = static_cast<uint32_t*>(ws);
-    m.dup = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + round_up(mask_bytes, 256));
-    m.dbuf = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(mask_bytes, 256) +
-                                      round_up(num_tokens * 4, 256));
-    m.num_words = (int32_t)words;
+    m.mask = static_cast<uint32_t*>(workspace);
+    m.dup = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + plan.dup_off);
+    m.dbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.d_off);
+    m.num_words = (int32_t)plan.words;
     hipLaunchKernelGGL(dsa::sparse_mla_bwd_prep_kernel, dim3((unsigned)num_tokens), dim3(256), 0, s, a, m);
-    hipLaunchKernelGGL(dsa::sparse_mla_bwd_kv_kernel, dim3((unsigned)((words + 1) / 2 * chunks)), dim3(256), 0, s, a,
-                       m);
+    hipLaunchKernelGGL(dsa::sparse_mla_bwd_kv_kernel, dim3((unsigned)((plan.words + 1) / 2 * plan.chunks)),
+                       dim3(256), 0, s, a, m);
     a.only = m.dup;   // rows with a repeated entry: token-major
     hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, s, a);
-    const bool launched = hipGetLastError() == hipSuccess;
-    const bool freed = hipFreeAsync(ws, s) == hipSuccess;
-    return launched && freed ? DSA_OK : DSA_ERR_HIP;
-  }
-  (void)hipGetLastError();   // a failed stream-ordered allocation: token-major below
-  if (hb == 16)
+  } else if (hb == 16) {
     hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, s, a);
+  }
   if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
+  return DSA_OK;
+}
+
+int dsa_sparse_mla_bwd_workspace_size(int64_t num_tokens, int32_t num_heads, int64_t num_kv, int32_t topk,
+                                      int32_t* schedule_out, int64_t* bytes_out) {
+  if (!bytes_out) return DSA_ERR_INVALID_ARGUMENT;
+  if (num_tokens < 0 || num_kv < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (num_heads < 1 || num_heads > DSA_MAX_HEADS || topk < 1 || topk > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+  BwdPlan plan;
+  bwd_plan(num_tokens, num_heads, num_kv, topk, &plan);
+  if (schedule_out) *schedule_out = plan.schedule;
+  *bytes_out = plan.ws_bytes;
   return DSA_OK;
 }
 

@@ -24,8 +24,10 @@
  *     dimension of q, kv, out is contiguous. bf16 pointers must be 16-byte
  *     aligned and bf16 strides multiples of 8 elements; lse must be 4-byte
  *     aligned.
- *   - Ownership: every buffer belongs to the caller. The library allocates
- *     nothing, keeps no pointer after it returns, and holds no state except a
+ *   - Ownership: every buffer belongs to the caller, scratch included (each
+ *     entry point that needs scratch has a workspace query and takes a
+ *     caller-provided workspace). The library allocates no device memory,
+ *     keeps no pointer after it returns, and holds no state except a
  *     per-device property cache filled once. Calls may come from several host
  *     threads.
  *   - Asynchrony: a call only enqueues kernels on `stream` (a hipStream_t;
@@ -182,21 +184,26 @@ int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stri
  *          16-byte aligned, dkv_stride_row a multiple of 4 and >= 576.
  * stream   hipStream_t to enqueue on.
  *
- * Two schedules, chosen from the sizes alone. Token-major: one workgroup per
- * token and head block adds each named row's gradient into dkv. kv-major,
- * when num_heads <= 16, 0 < num_kv <= 262144 and 3 * num_kv * num_heads <=
- * 256 * topk (rows that name a large share of kv, as in causal prefill): one
- * workgroup per (64 kv rows, 64-token chunk) keeps the rows' dkv in
- * registers and adds dq with atomics instead, so dq too may then differ in
- * the last bits between calls. Tokens whose row names some kv row twice go
- * to the token-major kernel within the same call. The kv-major schedule takes
- * ceil(num_kv/32) * num_tokens * 4 + ~68 * num_tokens bytes of scratch from
- * the device's default memory pool, stream-ordered (hipMallocAsync, freed with
- * hipFreeAsync on the same stream); if that allocation fails, or the scratch
- * would exceed 1 GiB, the call takes the token-major schedule.
- *
- * Limits: 1 <= num_heads <= 128, 1 <= topk <= 65536. dq and dkv must not
- * overlap the inputs or each other (checked on the host: DSA_ERR_INVALID_ARGUMENT).
+ * Two schedules, chosen from the sizes alone (dsa_sparse_mla_bwd_workspace_size
+ * reports which one a call takes). Token-major: one workgroup per token and
+ * head block adds each named row's gradient into dkv; it needs no workspace.
+ * kv-major, when num_heads <= 16, 0 < num_kv <= 262144 and 3 * num_kv *
+ * num_heads <= 256 * topk (rows that name a large share of kv, as in causal
+ * prefill), and its workspace is at most 1 GiB: one workgroup per (64 kv
+ * rows, 64-token chunk) keeps the rows' dkv in registers and adds dq with
+ * atomics instead, so dq too may then differ in the last bits between calls.
+ * Tokens whose row names some kv row twice go to the token-major kernel
+ * within the same call.
+ * workspace/workspace_bytes  device scratch owned by the caller, at least the
+ *          size dsa_sparse_mla_bwd_workspace_size reports for these sizes and
+ *          256-byte aligned; may be NULL/0 when that size is 0. Its contents
+ *          on entry do not matter; calls that share one workspace must be
+ *          stream-ordered. A smaller or misaligned workspace returns
+ *          DSA_ERR_WORKSPACE (the call never allocates and never changes
+ *          schedule because of the workspace).
+ * Limits: 1 <= num_heads <= 128, 1 <= topk <= 65536. dq, dkv and the
+ * workspace must not overlap the inputs or each other (checked on the host:
+ * DSA_ERR_INVALID_ARGUMENT).
  */
 int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
                        const void* kv, int64_t kv_stride_row, int64_t num_kv,
@@ -207,12 +214,40 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
                        const void* dout, int64_t dout_stride_tok, int64_t dout_stride_head,
                        float* dq, int64_t dq_stride_tok, int64_t dq_stride_head,
                        float* dkv, int64_t dkv_stride_row,
+                       void* workspace, int64_t workspace_bytes,
                        void* stream);
 
-/* Human-readable name of a dsa_status value (a static string). */
+/* Backward schedules reported by dsa_sparse_mla_bwd_workspace_size. */
+#define DSA_BWD_TOKEN_MAJOR 0
+#define DSA_BWD_KV_MAJOR 1
+
+/*
+ * Workspace query for dsa_sparse_mla_bwd. The pages that motivate it: the
+ * prime-rl pull request 4078 that adds a `cudnn_flashmla` DSA backend
+ * describes a backward that always failed because it did not provide the
+ * workspace its kernel required; here the caller learns the size up front.
+ *
+ * num_tokens, num_heads, num_kv, topk: as in the backward call.
+ * *schedule_out (may be NULL): DSA_BWD_TOKEN_MAJOR or DSA_BWD_KV_MAJOR, the
+ *   schedule a backward call with these sizes takes (on any device).
+ * *bytes_out: workspace bytes that call needs (0 for the token-major schedule).
+ * Returns DSA_OK, DSA_ERR_INVALID_ARGUMENT (negative sizes, NULL bytes_out) or
+ * DSA_ERR_UNSUPPORTED (num_heads or topk out of range).
+ */
+int dsa_sparse_mla_bwd_workspace_size(int64_t num_tokens, int32_t num_heads, int64_t num_kv,
+                                      int32_t topk, int32_t* schedule_out, int64_t* bytes_out);
+
+/* Human-readable name of a dsa_status value (a static string). The status
+ * codes carry the explicit rejections of unsupported paths that
+ * "feat: add XTuner TileLang sparse MLA backend" (lmdeploy PR 4904), Summary,
+ * describes. */
 const char* dsa_status_string(int status);
 
-/* 1 if HIP device `device` is a gfx950 (MI355X class) GPU, 0 if not or on error. */
+/* 1 if HIP device `device` is a gfx950 (MI355X class) GPU, 0 if not or on error.
+ * The runtime availability check that "[Feature] Add optional FlashMLA backend
+ * for DSA Sparse MLA" (xtuner PR 2083), Changes, performs before selecting its
+ * backend; here every entry point also returns DSA_ERR_UNSUPPORTED on other
+ * devices. */
 int dsa_device_supported(int device);
 
 /* Library version as major*10000 + minor*100 + patch. */

@@ -146,14 +146,14 @@ def _bwd(**over):
     args = dict(q=fake(0), q_st=8 * 576, q_sh=576, kv=fake(1), kv_st=576, num_kv=100, idx=fake(2),
                 idx_st=2048, T=8, H=8, topk=2048, sm=0.04, out=fake(3), o_st=8 * 512, o_sh=512,
                 lse=fake(4), lse_st=8, do=fake(5), do_st=8 * 512, do_sh=512, dq=fake(6), dq_st=8 * 576,
-                dq_sh=576, dkv=fake(7), dkv_st=576, stream=None)
+                dq_sh=576, dkv=fake(7), dkv_st=576, ws=None, ws_bytes=0, stream=None)
     args.update(over)
     a = args
     return dsa.lib().dsa_sparse_mla_bwd(
         a["q"], a["q_st"], a["q_sh"], a["kv"], a["kv_st"], a["num_kv"], a["idx"], a["idx_st"],
         a["T"], a["H"], a["topk"], a["sm"], a["out"], a["o_st"], a["o_sh"], a["lse"], a["lse_st"],
         a["do"], a["do_st"], a["do_sh"], a["dq"], a["dq_st"], a["dq_sh"], a["dkv"], a["dkv_st"],
-        a["stream"])
+        a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("over,status", [
@@ -182,6 +182,13 @@ def _bwd(**over):
     ({"sm": float("nan")}, INVALID),
     ({"sm": -1.0}, INVALID),
     ({"num_kv": -1}, INVALID),
+    ({"ws_bytes": -1}, INVALID),
+    # kv-major sizes (8 heads, 100 rows, topk 2048) need a workspace
+    ({"ws": None, "ws_bytes": 0}, WORKSPACE),
+    ({"ws": fake(8), "ws_bytes": 100}, WORKSPACE),            # too small
+    ({"ws": fake(8) + 16, "ws_bytes": 1 << 20}, WORKSPACE),   # not 256-byte aligned
+    ({"ws": fake(6), "ws_bytes": 1 << 20}, INVALID),          # over dq
+    ({"ws": fake(1), "ws_bytes": 1 << 20}, INVALID),          # over kv
 ])
 def test_bwd_host_validation(over, status):
     assert _bwd(**over) == status
@@ -197,7 +204,54 @@ def test_valid_call_reaches_the_device_check():
     assert _fwd() in (HIPERR, UNSUPPORTED)
     # out right after q (adjacent, not overlapping) passes the overlap check too
     assert _fwd(out=fake(0) + 2 * 8 * 8 * 576) in (HIPERR, UNSUPPORTED)
-    assert _bwd() in (HIPERR, UNSUPPORTED)
+    assert _bwd(ws=fake(8), ws_bytes=1 << 20) in (HIPERR, UNSUPPORTED)
+    # token-major sizes (64 heads) take no workspace
+    assert _bwd(H=64, q_st=64 * 576, o_st=64 * 512, lse_st=64, do_st=64 * 512,
+                dq_st=64 * 576) in (HIPERR, UNSUPPORTED)
+
+
+def _bwd_ws(T, H, N, topk):
+    return binding.bwd_workspace_size(T, H, N, topk)
+
+
+def _round256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("T,H,N,topk,schedule", [
+    (2119, 8, 2119, 2048, "kv-major"),        # SWE-like prefill rows
+    (150, 16, 200, 160, "kv-major"),
+    (150, 17, 200, 160, "token-major"),        # more than 16 heads
+    (8192, 64, 8192, 2048, "token-major"),
+    (100, 8, 5000, 64, "token-major"),         # sparse rows: 3 N H > 256 topk
+    (3, 1, 262144, 3072, "kv-major"),          # 3 N H = 256 topk, the whole LDS bitmap
+    (3, 1, 262145, 3072, "token-major"),       # one row more than the bitmap holds
+    (0, 8, 100, 2048, "token-major"),          # no tokens
+    (10, 8, 0, 2048, "token-major"),           # no kv rows
+])
+def test_bwd_workspace_query(T, H, N, topk, schedule):
+    """The schedule comes from the sizes alone, and the kv-major workspace is
+    the occupancy masks, the repeat flags and D, each 256-byte aligned."""
+    got, nbytes = _bwd_ws(T, H, N, topk)
+    assert got == schedule
+    if schedule == "kv-major":
+        words = (N + 31) // 32
+        assert nbytes == _round256(words * T * 4) + _round256(T * 4) + T * 64
+    else:
+        assert nbytes == 0
+
+
+def test_bwd_workspace_cap():
+    """Above 1 GiB of masks the token-major schedule runs instead."""
+    T, N = 65536, 131072   # 4096 words x 65536 tokens x 4 bytes = 1 GiB of masks alone
+    assert _bwd_ws(T, 1, N, 65536)[0] == "token-major"
+    assert _bwd_ws(T // 2, 1, N, 65536)[0] == "kv-major"
+
+
+def test_bwd_workspace_query_rejects_bad_sizes():
+    for args in ((-1, 8, 10, 10), (10, 8, -1, 10), (10, 0, 10, 10), (10, 8, 10, 0)):
+        with pytest.raises(binding.DsaError):
+            _bwd_ws(*args)
 
 
 @pytest.mark.parametrize("T,H,topk,req,splits,nbytes", [

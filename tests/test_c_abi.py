@@ -33,9 +33,14 @@ int main(void) {
       != DSA_ERR_INVALID_ARGUMENT)
     bad |= 8;
   /* unsupported head count, before any pointer is looked at */
-  if (dsa_sparse_mla_bwd(0, 0, 0, 0, 0, 0, 0, 0, 4, 129, 2048, 0.04f, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0)
-      != DSA_ERR_UNSUPPORTED)
+  if (dsa_sparse_mla_bwd(0, 0, 0, 0, 0, 0, 0, 0, 4, 129, 2048, 0.04f, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0,
+                         0, 0) != DSA_ERR_UNSUPPORTED)
     bad |= 16;
+  int32_t sched = -1;
+  int64_t bwd_bytes = -1;
+  if (dsa_sparse_mla_bwd_workspace_size(2119, 8, 2119, 2048, &sched, &bwd_bytes) != DSA_OK ||
+      sched != DSA_BWD_KV_MAJOR || bwd_bytes <= 0)
+    bad |= 64;
   int32_t splits = -1;
   int64_t bytes = -1;
   if (dsa_sparse_mla_workspace_size(100, 8, 2048, 1, &splits, &bytes) != DSA_OK || splits != 1 || bytes != 0)

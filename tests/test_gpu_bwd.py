@@ -77,11 +77,11 @@ def run(q, kv, idx, sm, dout, own_forward=False):
     return dq, dkv
 
 
-def kv_major(H, N, topk):
-    """The library's choice of the kv-major pass (stated with the backward in
-    include/dsa_sparse_mla.h): at most 16 heads, at most 262144 kv rows, and
+def kv_major(H, N, topk, T=64):
+    """The schedule the library reports for these sizes (its workspace query):
+    the kv-major pass takes at most 16 heads, at most 262144 kv rows, and
     topk at least 3/256 of H x num_kv."""
-    return H <= 16 and 0 < N <= 32 * 8192 and 3 * N * H <= 256 * topk
+    return _dsa().bwd_workspace_size(T, H, N, topk)[0] == "kv-major"
 
 
 def ref(q, kv, idx, sm, dout):
