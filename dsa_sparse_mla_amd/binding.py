@@ -66,6 +66,10 @@ def lib() -> ctypes.CDLL:
             vp, i64,                 # lse
             i32, vp, i64,            # num_splits, workspace, bytes
             vp]                      # stream
+        L.dsa_sparse_mla_fwd_paged_noalloc.restype = ctypes.c_int
+        # the paged arguments up to num_splits, without workspace/bytes
+        L.dsa_sparse_mla_fwd_paged_noalloc.argtypes = L.dsa_sparse_mla_fwd_paged.argtypes[:-3] + [
+            vp]                      # stream
         L.dsa_sparse_mla_bwd.restype = ctypes.c_int
         L.dsa_sparse_mla_bwd.argtypes = [
             vp, i64, i64,            # q
@@ -227,6 +231,44 @@ def sparse_mla_fwd_paged(q, kv_pages, page_table, seq_lens, indices, sm_scale, q
             stream)
     if st != 0:
         raise DsaError(st, "dsa_sparse_mla_fwd_paged")
+    return out, lse
+
+
+def sparse_mla_fwd_paged_noalloc(q, kv_pages, page_table, seq_lens, indices, sm_scale, q_per_seq,
+                                 out, lse, num_splits=0):
+    """sparse_mla_fwd_paged for callers that cannot allocate: out and lse are
+    required, and the split partials go to the library's own fixed-size
+    device scratch (DSA_NOALLOC_SCRATCH_BYTES per GPU) instead of a workspace.
+    Calls on one GPU that may overlap in time race on that scratch."""
+    dev = q.device
+    _check(q, "q", torch.bfloat16, 3, dev)
+    _check(kv_pages, "kv_pages", torch.bfloat16, 3, dev)
+    _check(page_table, "page_table", torch.int32, 2, dev)
+    _check(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _check(indices, "indices", torch.int32, 2, dev)
+    T, H, D = q.shape
+    S = page_table.shape[0]
+    if D != DQK or kv_pages.shape[2] != DQK:
+        raise ValueError("q and kv rows must be 576 wide")
+    if seq_lens.shape[0] != S or T != S * q_per_seq or indices.shape[0] != T:
+        raise ValueError("need num_seqs * q_per_seq query tokens and one seq_len per sequence")
+    if out is None or lse is None:
+        raise ValueError("out and lse must be given (this entry point allocates nothing)")
+    out, lse = _outputs(q, T, H, out, lse)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib().dsa_sparse_mla_fwd_paged_noalloc(
+            q.data_ptr(), q.stride(0), q.stride(1),
+            kv_pages.data_ptr(), kv_pages.stride(0), kv_pages.stride(1),
+            kv_pages.shape[0], kv_pages.shape[1],
+            page_table.data_ptr(), page_table.stride(0), page_table.shape[1], seq_lens.data_ptr(),
+            indices.data_ptr(), indices.stride(0),
+            S, int(q_per_seq), H, indices.shape[1], float(sm_scale),
+            out.data_ptr(), out.stride(0), out.stride(1),
+            lse.data_ptr(), lse.stride(0),
+            int(num_splits), stream)
+    if st != 0:
+        raise DsaError(st, "dsa_sparse_mla_fwd_paged_noalloc")
     return out, lse
 
 

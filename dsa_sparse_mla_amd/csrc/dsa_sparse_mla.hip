@@ -147,6 +147,28 @@ int device_check() {
   return d->gfx950 ? DSA_OK : DSA_ERR_UNSUPPORTED;
 }
 
+// Scratch of dsa_sparse_mla_fwd_paged_noalloc: the split partials live in
+// this file-scope device array instead of a caller workspace. Each device
+// holds its own copy at its own address; host code uses only the address
+// that hipGetSymbolAddress returns for the current device (the array's name
+// on the host is a stand-in, not a device pointer).
+static __device__ __align__(256) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+void* g_scratch_ptr[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// The device address of `scratch` on device `dev` (which must be current),
+// looked up once per device; nullptr if the lookup failed.
+void* scratch_address(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[dev] = ptr;
+    else (void)hipGetLastError();
+  });
+  return g_scratch_ptr[dev];
+}
+
 // Backward schedule and workspace, from the sizes alone.
 //
 // kv-major when the rows are dense enough: per (token, 64 kv rows) it adds
@@ -371,6 +393,28 @@ int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stri
   st = device_check();
   if (st != DSA_OK) return st;
   return launch<true>(a, static_cast<hipStream_t>(stream));
+}
+
+int dsa_sparse_mla_fwd_paged_noalloc(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                                     const void* kv_pages, int64_t kv_stride_page, int64_t kv_stride_row,
+                                     int64_t num_pages, int32_t page_size, const int32_t* page_table,
+                                     int64_t page_table_stride, int32_t max_pages_per_seq,
+                                     const int32_t* seq_lens, const int32_t* indices, int64_t idx_stride_tok,
+                                     int32_t num_seqs, int32_t q_per_seq, int32_t num_heads, int32_t topk,
+                                     float sm_scale, void* out, int64_t out_stride_tok,
+                                     int64_t out_stride_head, float* lse, int64_t lse_stride_tok,
+                                     int32_t num_splits, void* stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_HIP;
+  void* ws = scratch_address(dev);
+  if (!ws) return DSA_ERR_HIP;
+  // the paged entry point validates everything and returns DSA_ERR_WORKSPACE
+  // when the split partials of this call would not fit the array
+  return dsa_sparse_mla_fwd_paged(q, q_stride_tok, q_stride_head, kv_pages, kv_stride_page, kv_stride_row,
+                                  num_pages, page_size, page_table, page_table_stride, max_pages_per_seq,
+                                  seq_lens, indices, idx_stride_tok, num_seqs, q_per_seq, num_heads, topk,
+                                  sm_scale, out, out_stride_tok, out_stride_head, lse, lse_stride_tok,
+                                  num_splits, ws, DSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_head, const void* kv,

@@ -156,6 +156,38 @@ int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stri
                              void* stream);
 
 /*
+ * dsa_sparse_mla_fwd_paged without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, and harnesses that forbid allocation. The split partials go to a
+ * scratch array of DSA_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on (from the module's load until the process ends); the call
+ * itself allocates nothing.
+ *
+ * Arguments, limits and results are those of dsa_sparse_mla_fwd_paged,
+ * without workspace/workspace_bytes. A call whose split partials
+ * (num_seqs * q_per_seq * splits * num_heads * 2056 bytes, splits as the
+ * workspace query reports) exceed DSA_NOALLOC_SCRATCH_BYTES returns
+ * DSA_ERR_WORKSPACE and launches nothing; num_splits = 1 needs no scratch.
+ * Every slot of the array that a call reads is written earlier in the same
+ * call, so nothing needs clearing between calls. All calls on one GPU share
+ * that GPU's array: calls that may overlap in time on one GPU (different
+ * streams without ordering, or several host threads) race on it and must be
+ * serialised by the caller.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (32 << 20)
+int dsa_sparse_mla_fwd_paged_noalloc(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                                     const void* kv_pages, int64_t kv_stride_page, int64_t kv_stride_row,
+                                     int64_t num_pages, int32_t page_size,
+                                     const int32_t* page_table, int64_t page_table_stride,
+                                     int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                     const int32_t* indices, int64_t idx_stride_tok,
+                                     int32_t num_seqs, int32_t q_per_seq, int32_t num_heads,
+                                     int32_t topk, float sm_scale,
+                                     void* out, int64_t out_stride_tok, int64_t out_stride_head,
+                                     float* lse, int64_t lse_stride_tok,
+                                     int32_t num_splits, void* stream);
+
+/*
  * Sparse MLA backward over a flat KV array: the gradients of the forward's
  * output O with respect to q and kv, for an upstream gradient dout.
  * Pages: xtuner PR 2083, Motivation (the forward's output and LSE feed the
