@@ -1,4 +1,4 @@
-"""CPU oracle for the DSA sparse MLA forward and backward.
+"""CPU oracle for the DSA sparse MLA forward and backward, and the top-k index selection.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import this package:
 only the test suite, the smoke check and the CPU-baseline leg of the benchmark
@@ -12,3 +12,4 @@ from .sparse_mla_ref import (  # noqa: F401
     sparse_mla_fwd_paged_ref,
 )
 from .bwd_ref import sparse_mla_bwd_ref  # noqa: F401,E402
+from .topk_ref import topk_indices_ref  # noqa: F401,E402

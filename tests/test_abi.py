@@ -38,6 +38,27 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, name), f"missing export {name}"
 
 
+def declared_arg_counts():
+    """Parameter count of every function the header declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    counts = {}
+    for name, params in re.findall(r"\b(dsa_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = params.strip()
+        counts[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return counts
+
+
+def test_binding_prototypes_match_the_header():
+    """Each ctypes prototype has as many arguments as the header's declaration."""
+    L = dsa.lib()
+    counts = declared_arg_counts()
+    assert set(counts) == set(declared_functions())
+    for name, n in counts.items():
+        fn = getattr(L, name)
+        assert fn.argtypes is not None, f"{name} has no ctypes prototype"
+        assert len(fn.argtypes) == n, f"{name}: binding has {len(fn.argtypes)} arguments, header {n}"
+
+
 def test_single_hip_runtime_mapped():
     import torch  # noqa: F401
     dsa.lib()

@@ -223,3 +223,45 @@ def make(name: str, device="cpu", **kw):
     if WORKLOADS[name].kind == "paged":
         return make_paged(device=device, **kw)
     return make_flat(name, device=device, **kw)
+
+
+# ---------------------------------------------------------------- index selection inputs
+
+def causal_ranges(cu_seqlens, num_tokens: int):
+    """Candidate ranges of packed causal prefill: token t at position p of the
+    document that starts at row d0 may select rows d0 .. d0 + p (itself
+    included), as key_start[t] = d0, key_end[t] = d0 + p + 1. Without
+    documents (cu_seqlens None) the whole batch is one document."""
+    if cu_seqlens is None:
+        cu = np.array([0, num_tokens], dtype=np.int64)
+    else:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+    ks = np.zeros(num_tokens, dtype=np.int32)
+    ke = np.zeros(num_tokens, dtype=np.int32)
+    for d in range(len(cu) - 1):
+        a, b = int(cu[d]), int(cu[d + 1])
+        ks[a:b] = a
+        ke[a:b] = np.arange(a + 1, b + 1)
+    return torch.from_numpy(ks), torch.from_numpy(ke)
+
+
+def index_scores(num_tokens: int, num_cols: int, seed: int, device="cpu", kind="normal"):
+    """Stand-in indexer scores, fp32 [num_tokens, num_cols] (the pages do not
+    define the score function). kind "normal": N(0,1) from
+    torch.Generator(seed); "ties": integers 0..7 drawn the same way (many
+    equal scores per row); "special": normal draws with about 1% each of
+    +inf, -inf, NaN, +0 and -0 planted by numpy.random.default_rng(seed)."""
+    gen = torch.Generator(device=device).manual_seed(int(seed))
+    s = torch.randn((num_tokens, num_cols), generator=gen, device=device, dtype=torch.float32)
+    if kind == "ties":
+        s = torch.floor(s * 2.0 + 4.0).clamp_(0.0, 7.0)
+    elif kind == "special":
+        rng = np.random.default_rng(seed)
+        u = rng.random((num_tokens, num_cols))
+        host = s.cpu().numpy()
+        for i, v in enumerate((np.inf, -np.inf, np.nan, 0.0, -0.0)):
+            host[(u >= 0.01 * i) & (u < 0.01 * (i + 1))] = v
+        s = torch.from_numpy(host).to(device)
+    elif kind != "normal":
+        raise KeyError(kind)
+    return s
