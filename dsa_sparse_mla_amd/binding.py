@@ -89,6 +89,13 @@ def lib() -> ctypes.CDLL:
         L.dsa_sparse_mla_workspace_size.restype = ctypes.c_int
         L.dsa_sparse_mla_workspace_size.argtypes = [i64, i32, i32, i32,
                                                     ctypes.POINTER(i32), ctypes.POINTER(i64)]
+        L.dsa_topk_indices.restype = ctypes.c_int
+        L.dsa_topk_indices.argtypes = [
+            vp, i64, i64,            # scores, row stride, num_cols
+            vp, vp,                  # key_start, key_end
+            i64, i32,                # num_tokens, topk
+            vp, i64,                 # indices, row stride
+            vp]                      # stream
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_status_string.argtypes = [ctypes.c_int]
         L.dsa_device_supported.restype = ctypes.c_int
@@ -270,6 +277,48 @@ def sparse_mla_fwd_paged_noalloc(q, kv_pages, page_table, seq_lens, indices, sm_
     if st != 0:
         raise DsaError(st, "dsa_sparse_mla_fwd_paged_noalloc")
     return out, lse
+
+
+def topk_indices(scores, key_start, key_end, topk, indices=None, num_cols=None):
+    """Top-k index rows from indexer scores (dsa_topk_indices).
+
+    scores [T, num_cols] fp32 (or None when no row has more than topk
+    candidates); key_start, key_end [T] int32: token t's candidates are the
+    columns key_start[t] <= j < key_end[t]. Returns indices [T, topk] int32:
+    the selected columns ascending, then -1. Rows with at most topk
+    candidates select all of them without reading scores.
+    """
+    dev = key_start.device
+    _check(key_start, "key_start", torch.int32, 1, dev)
+    _check(key_end, "key_end", torch.int32, 1, dev)
+    T = key_start.shape[0]
+    if key_end.shape[0] != T:
+        raise ValueError("key_start and key_end need one entry per token")
+    if scores is not None:
+        _check(scores, "scores", torch.float32, 2, dev)
+        if scores.shape[0] != T:
+            raise ValueError("scores need one row per token")
+        if num_cols is None:
+            num_cols = scores.shape[1]
+        elif num_cols != scores.shape[1]:
+            raise ValueError("num_cols differs from the score rows")
+    elif num_cols is None:
+        raise ValueError("num_cols is needed without scores")
+    if indices is None:
+        indices = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    _check(indices, "indices", torch.int32, 2, dev)
+    if tuple(indices.shape) != (T, topk):
+        raise ValueError("indices must be [T, topk]")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib().dsa_topk_indices(
+            scores.data_ptr() if scores is not None else None,
+            scores.stride(0) if scores is not None else 0, int(num_cols),
+            key_start.data_ptr(), key_end.data_ptr(), T, int(topk),
+            indices.data_ptr(), indices.stride(0), stream)
+    if st != 0:
+        raise DsaError(st, "dsa_topk_indices")
+    return indices
 
 
 def sparse_mla_bwd(q, kv, indices, sm_scale, out, lse, dout, dq=None, dkv=None, workspace=None):

@@ -16,6 +16,7 @@
 #include "fwd_kernel.hpp"
 #include "fwd_kernel_ws.hpp"
 #include "bwd_kernel.hpp"
+#include "topk_kernel.hpp"
 
 namespace {
 
@@ -537,6 +538,44 @@ int dsa_sparse_mla_bwd_workspace_size(int64_t num_tokens, int32_t num_heads, int
   bwd_plan(num_tokens, num_heads, num_kv, topk, &plan);
   if (schedule_out) *schedule_out = plan.schedule;
   *bytes_out = plan.ws_bytes;
+  return DSA_OK;
+}
+
+int dsa_topk_indices(const float* scores, int64_t score_stride_tok, int64_t num_cols,
+                     const int32_t* key_start, const int32_t* key_end, int64_t num_tokens, int32_t topk,
+                     int32_t* indices, int64_t idx_stride_tok, void* stream) {
+  if (num_tokens < 0 || num_cols < 0 || score_stride_tok < 0 || idx_stride_tok < 0)
+    return DSA_ERR_INVALID_ARGUMENT;
+  if (topk < 1 || topk > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+  if (num_cols > INT32_MAX) return DSA_ERR_UNSUPPORTED;   // column ids are int32
+  if (num_tokens == 0) return DSA_OK;
+  if (num_tokens >= ((int64_t)1 << 31)) return DSA_ERR_UNSUPPORTED;   // one workgroup per row
+  if (!key_start || !key_end || !indices) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned(key_start, 4) || !aligned(key_end, 4) || !aligned(indices, 4)) return DSA_ERR_INVALID_ARGUMENT;
+  if (num_tokens > 1 && idx_stride_tok < topk) return DSA_ERR_INVALID_ARGUMENT;
+  if (scores) {
+    if (!aligned(scores, 4)) return DSA_ERR_INVALID_ARGUMENT;
+    if (num_tokens > 1 && score_stride_tok < num_cols) return DSA_ERR_INVALID_ARGUMENT;
+  }
+  int st = check_overlaps({extent2(indices, num_tokens, idx_stride_tok, topk, 4)},
+                          {extent2(scores, num_tokens, score_stride_tok, num_cols, 4),
+                           extent2(key_start, 1, 0, num_tokens, 4), extent2(key_end, 1, 0, num_tokens, 4)});
+  if (st != DSA_OK) return st;
+  st = device_check();
+  if (st != DSA_OK) return st;
+  dsa::TopkArgs a;
+  a.scores = scores;
+  a.score_st = score_stride_tok;
+  a.num_cols = num_cols;
+  a.key_start = key_start;
+  a.key_end = key_end;
+  a.num_tokens = num_tokens;
+  a.topk = topk;
+  a.out = indices;
+  a.out_st = idx_stride_tok;
+  hipLaunchKernelGGL(dsa::topk_select_kernel, dim3((unsigned)num_tokens), dim3(dsa::kTkThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
   return DSA_OK;
 }
 

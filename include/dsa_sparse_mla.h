@@ -269,6 +269,44 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
 int dsa_sparse_mla_bwd_workspace_size(int64_t num_tokens, int32_t num_heads, int64_t num_kv,
                                       int32_t topk, int32_t* schedule_out, int64_t* bytes_out);
 
+/*
+ * Top-k index selection: turns each query token's row of indexer scores into
+ * the -1-padded index row that the sparse forward consumes.
+ * Pages: "feat: add XTuner TileLang sparse MLA backend" (lmdeploy PR 4904),
+ * Summary (DSA index production kept for short prefill) and per-file overview
+ * (prefill scores computed over chunks of query rows; the short-prefill
+ * scoring skip); Validation (-1-padded index rows); "[Feature] Add optional
+ * FlashMLA backend for DSA Sparse MLA" (xtuner PR 2083), Changes (an indexer
+ * in front of the sparse kernel). The score function is the caller's.
+ *
+ * scores     fp32 [num_tokens, num_cols]; (t, j) at scores + t*score_stride_tok + j.
+ *            May be NULL when no row has more than topk candidates (then no
+ *            score is read; see below).
+ * key_start, key_end  int32 [num_tokens]: token t's candidates are columns
+ *            key_start[t] <= j < key_end[t], clipped to [0, num_cols); an
+ *            empty range selects nothing. Packed causal prefill: the token's
+ *            document start and its own row + 1 (column = global kv row);
+ *            decode: 0 and the context length (column = logical position).
+ * indices    int32 [num_tokens, topk] (written); row t at indices + t*idx_stride_tok.
+ *
+ * Row t holds the selected column ids in ascending order, then -1:
+ *   - at most topk candidates: all of them, and the row's scores are never
+ *     read (the short-prefill skip: such rows need no scoring at all);
+ *   - otherwise the topk candidates first in this order: larger score; for
+ *     equal scores (-0 equals +0) the smaller column; NaN after every number
+ *     (NaNs among themselves by column).
+ *   - with scores NULL a row of more than topk candidates selects nothing.
+ * The result is exact and deterministic (integer work, no tolerance).
+ *
+ * Limits: 1 <= topk <= 65536, num_cols <= 2^31 - 1, num_tokens < 2^31.
+ * indices must not overlap scores, key_start or key_end (DSA_ERR_INVALID_ARGUMENT).
+ */
+int dsa_topk_indices(const float* scores, int64_t score_stride_tok, int64_t num_cols,
+                     const int32_t* key_start, const int32_t* key_end,
+                     int64_t num_tokens, int32_t topk,
+                     int32_t* indices, int64_t idx_stride_tok,
+                     void* stream);
+
 /* Human-readable name of a dsa_status value (a static string). The status
  * codes carry the explicit rejections of unsupported paths that
  * "feat: add XTuner TileLang sparse MLA backend" (lmdeploy PR 4904), Summary,

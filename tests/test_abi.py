@@ -317,3 +317,44 @@ def test_workspace_query_rejects_bad_sizes():
         binding.workspace_size(10, 0, 2048, 0)
     with pytest.raises(binding.DsaError):
         binding.workspace_size(10, 8, 5000, 1)
+
+
+def _topk(**over):
+    args = dict(scores=fake(0), s_st=5000, C=5000, ks=fake(1), ke=fake(2), T=8, topk=2048,
+                idx=fake(3), idx_st=2048, stream=None)
+    args.update(over)
+    a = args
+    return dsa.lib().dsa_topk_indices(a["scores"], a["s_st"], a["C"], a["ks"], a["ke"], a["T"], a["topk"],
+                                      a["idx"], a["idx_st"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"T": -1}, INVALID),
+    ({"C": -1}, INVALID),
+    ({"s_st": -1}, INVALID),
+    ({"idx_st": -1}, INVALID),
+    ({"topk": 0}, UNSUPPORTED),
+    ({"topk": 65537}, UNSUPPORTED),
+    ({"C": 1 << 31}, UNSUPPORTED),          # column ids are int32
+    ({"T": 0}, OK),                         # an empty batch is a no-op
+    ({"T": 0, "idx": None, "ks": None}, OK),
+    ({"ks": None}, INVALID),
+    ({"ke": None}, INVALID),
+    ({"idx": None}, INVALID),
+    ({"idx": fake(3) + 2}, INVALID),        # not 4-byte aligned
+    ({"scores": fake(0) + 2}, INVALID),
+    ({"idx_st": 2047}, INVALID),            # index rows overlap
+    ({"s_st": 4999}, INVALID),              # score rows overlap
+    ({"idx": fake(0) + 64}, INVALID),       # indices inside the scores
+    ({"idx": fake(1)}, INVALID),            # indices over key_start
+])
+def test_topk_host_validation(over, status):
+    assert _topk(**over) == status
+
+
+def test_topk_valid_call_reaches_the_device_check():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _topk() in (HIPERR, UNSUPPORTED)
+    assert _topk(scores=None, s_st=0) in (HIPERR, UNSUPPORTED)   # no scores is allowed

@@ -169,6 +169,26 @@ def make_flat(name: str, device="cpu", layout=None, num_tokens=None, num_heads=N
     return out
 
 
+def _decode_lengths(rng, num_seqs, lo, hi):
+    return rng.integers(lo, hi + 1, size=num_seqs).astype(np.int64)
+
+
+def decode_lengths():
+    """Cached lengths L_b of the decode workload's sequences (the first draw
+    of its recipe), without building its cache."""
+    w = WORKLOADS["decode"]
+    e = w.extra
+    return _decode_lengths(np.random.default_rng(w.seed), e["num_seqs"], e["min_len"], e["max_len"])
+
+
+def varlen_cu_seqlens(name: str):
+    """Document boundaries of a packed workload (the first draw of its
+    recipe), without building its tensors."""
+    w = WORKLOADS[name]
+    cu, _ = document_starts(np.random.default_rng(w.seed), w.num_tokens)
+    return cu
+
+
 def make_paged(device="cpu", num_seqs=None, q_per_seq=None, num_heads=None, topk=None,
                page_size=None, min_len=None, max_len=None, seed=None, max_pages=None):
     """Inputs of the paged-decode workload; sizes may be overridden for tests.
@@ -191,7 +211,7 @@ def make_paged(device="cpu", num_seqs=None, q_per_seq=None, num_heads=None, topk
     hi = e["max_len"] if max_len is None else int(max_len)
     s = w.seed if seed is None else int(seed)
     rng = np.random.default_rng(s)
-    lens = rng.integers(lo, hi + 1, size=B).astype(np.int64)
+    lens = _decode_lengths(rng, B, lo, hi)
     npages = -(-lens // ps)
     P = int(npages.sum())
     mp = int(-(-hi // ps)) if max_pages is None else int(max_pages)
