@@ -61,7 +61,7 @@ def source_hash() -> str:
 
 def traffic_path(workload: str, op: str = "fwd") -> str:
     return os.path.join(ROOT, "profiles", f"traffic_{workload}.json" if op == "fwd"
-                        else f"traffic_bwd_{workload}.json")
+                        else f"traffic_{op}_{workload}.json")
 
 
 def traffic_for(workload: str, op: str = "fwd"):
@@ -83,6 +83,10 @@ FWD_KERNEL = re.compile(r"sparse_mla_fwd(_ws)?_kernel")   # the forward kernels'
 # prepass and pass, and the token-major kernel
 BWD_KERNEL = re.compile(r"dkv_zero_kernel|sparse_mla_bwd_(prep_|kv_)?kernel")
 BWD_CALL_MARK = re.compile(r"dkv_zero_kernel")
+TOPK_KERNEL = re.compile(r"topk_select_kernel")
+OP_KERNEL = {"fwd": FWD_KERNEL, "bwd": BWD_KERNEL, "topk": TOPK_KERNEL}
+# file-name stem of each op's profiles
+OP_STEM = {"fwd": "sparse_mla_fwd", "bwd": "sparse_mla_bwd", "topk": "dsa_topk"}
 
 
 def copy_calibration(dev, reps: int = 3):
@@ -120,13 +124,13 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: st
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         vals = per_dispatch(path, counter)
         copy = [v for (d, k), v in vals.items() if "neg" in k]
-        kern = FWD_KERNEL if op == "fwd" else BWD_KERNEL
+        kern = OP_KERNEL[op]
         fwd = [v for (d, k), v in vals.items() if kern.search(k)]
         if not copy or not fwd:
             raise SystemExit(f"{path}: no calibration copy or {op} dispatch with {counter}")
         factor = COPY_BYTES / (statistics.median(copy) * 1024.0)
-        if op == "fwd":
-            # one forward kernel per launch: the median dispatch
+        if op != "bwd":
+            # one kernel per launch: the median dispatch
             kib, count = statistics.median(fwd), len(fwd)
         else:
             # a backward call launches several kernels: their sum per call
@@ -146,6 +150,111 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: st
     print(json.dumps(out))
 
 
+def _bench_line(log_path: str) -> dict:
+    with open(log_path) as f:
+        lines = [ln for ln in f if ln.startswith("{")]
+    if not lines:
+        raise SystemExit(f"{log_path}: no JSON line from bench.py")
+    return json.loads(lines[-1])
+
+
+def _profile_args(args, rec) -> str:
+    op = "" if args.op == "fwd" else f" --op {args.op}"
+    return (f"python bench.py{op} --workload {args.workload} --steps {rec['steps']} --warmup {rec['warmup']} "
+            "--cpu-budget 0 --no-legs")
+
+
+def summarize_trace(args, trace_dir: str, log_path: str, out_dir: str | None = None):
+    """Format a rocprofv3 kernel-trace run of this script (-d trace_dir -o kt)
+    into profiles/<op>_<workload>_kernel_trace.md: the command, the per-kernel
+    statistics, the per-dispatch durations of the timed launches and the
+    script's own line from the same run (its HIP-event average must agree)."""
+    import csv
+    import statistics
+    rec = _bench_line(log_path)
+    steps = rec["steps"]
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "kt_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(trace_dir, "kt_kernel_trace.csv"))))
+    cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o kt -- "
+           + _profile_args(args, rec))
+    cfg = rec["config"]
+
+    def short(n):
+        return n if len(n) <= 70 else n[:67] + "..."
+    out = [f"# {OP_STEM[args.op]} kernel trace: {cfg['workload']}", "",
+           "MI355X (gfx950), one GPU. Command (from the repository root):", "", "```", cmd, "```", "",
+           f"Kernel sources hash (bench.py `source_hash`): `{rec['source_hash']}`", "",
+           "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in stats[:8]:
+        out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    out += ["", "The calls include the warm-up launches; torch kernels are input generation.",
+            "Per-dispatch durations of the library's kernels, timed launches only (`kt_kernel_trace.csv`):", ""]
+    by = {}
+    for r in trace:
+        by.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    for k, v in by.items():
+        if "dsa::" in k:
+            t = v[-steps:]
+            out.append(f"* `{short(k)}`: {statistics.mean(t):.1f} us average over the last {len(t)} launches "
+                       f"(min {min(t):.1f}, max {max(t):.1f})")
+    r = rec["roofline"]
+    out += ["", "bench.py's line from the same run (HIP events on the launch stream, timed steps only):", "",
+            f"* event average {rec['kernel_ms_avg'] * 1e3:.1f} us per step, wall {rec['ms_per_step'] * 1e3:.1f} us per step",
+            f"* configuration: `{json.dumps(cfg)}`",
+            f"* roofline: {r['bound']} {r['achieved']} {r['unit']} of {r['peak']} = {r['frac']}"]
+    if "tflops" in rec:
+        out.append(f"* {rec['gathered_kv_gbps']} GB/s of gathered rows, {rec['tflops']} TFLOP/s (wall time)")
+    tp = traffic_path(args.workload, args.op)
+    if os.path.exists(tp):
+        t = json.load(open(tp))
+        if t["source_hash"] == rec["source_hash"]:
+            out += ["", f"HBM traffic per call (`profiles/{os.path.basename(tp)}`, two counter runs scaled by a "
+                    f"copy of known size): fetch {t['fetch_bytes'] / 1e6:.1f} MB, write {t['write_bytes'] / 1e6:.1f} MB."]
+    name = f"{OP_STEM[args.op]}_{args.workload}_kernel_trace.md"
+    with open(os.path.join(out_dir or os.path.join(ROOT, "profiles"), name), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("wrote " + name)
+
+
+def summarize_counters(args, csv_paths, out_dir: str | None = None):
+    """Median per dispatch of every counter in rocprofv3 --pmc CSVs, for the
+    op's kernel, into profiles/counters_<op>_<workload>.json, with derived
+    MFMA-busy and L2 hit fractions. SQ_VALU_MFMA_BUSY_CYCLES is compared with
+    GRBM_GUI_ACTIVE (the dispatch's GPU cycles) x 1024 SIMDs."""
+    import csv
+    import statistics
+    kern = OP_KERNEL[args.op]
+    per = {}
+    names = set()
+    for path in csv_paths:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if not kern.search(row.get("Kernel_Name", "")):
+                    continue
+                key = (path, row["Dispatch_Id"])
+                c = row["Counter_Name"]
+                names.add(row["Kernel_Name"])
+                per.setdefault(c, {}).setdefault(key, 0.0)
+                per[c][key] += float(row["Counter_Value"])
+    if not per:
+        raise SystemExit("no dispatch of the op's kernel in the counter files")
+    med = {c: statistics.median(v.values()) for c, v in per.items()}
+    out = {"workload": args.workload, "op": args.op, "source_hash": source_hash(),
+           "kernels": sorted(names), "dispatches": {c: len(v) for c, v in per.items()}, "counters": med,
+           "command": args.traffic_command}
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and med.get("GRBM_GUI_ACTIVE"):
+        out["mfma_busy_frac"] = round(med["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024.0 * med["GRBM_GUI_ACTIVE"]), 4)
+    hit, miss = med.get("TCC_HIT_sum"), med.get("TCC_MISS_sum")
+    if hit is not None and miss is not None and hit + miss > 0:
+        out["l2_hit_frac"] = round(hit / (hit + miss), 4)
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"counters_{args.op}_{args.workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def valid_keys(d) -> int:
     import torch
     if "kv" in d:
@@ -159,7 +268,7 @@ def valid_keys(d) -> int:
     return int(((idx >= 0) & (idx < lens)).sum().item())   # the decode tables map every position
 
 
-def cpu_baseline(d, budget_s: float):
+def cpu_baseline(d, budget_s: float, dtype="float64"):
     """Time the CPU oracle on the last tokens of the workload until ~budget_s."""
     import numpy as np
     from oracle import sparse_mla_fwd_paged_ref, sparse_mla_fwd_ref
@@ -187,14 +296,14 @@ def cpu_baseline(d, budget_s: float):
             a, b = s0 * Q, s1 * Q
             t0 = time.perf_counter()
             sparse_mla_fwd_paged_ref(q[a:b], kvp, table[s0:s1], lens[s0:s1], idx[a:b],
-                                     d["sm_scale"], Q)
+                                     d["sm_scale"], Q, dtype=getattr(np, dtype))
             elapsed += time.perf_counter() - t0
             seq = np.arange(a, b) // Q - s0
             done_keys += int(((idx[a:b] >= 0) & (idx[a:b] < lens[s0:s1][seq][:, None])).sum())
         else:
             a, b = max(0, t_end - chunk), t_end
             t0 = time.perf_counter()
-            sparse_mla_fwd_ref(q[a:b], kv, idx[a:b], d["sm_scale"])
+            sparse_mla_fwd_ref(q[a:b], kv, idx[a:b], d["sm_scale"], dtype=getattr(np, dtype))
             elapsed += time.perf_counter() - t0
             done_keys += int(((idx[a:b] >= 0) & (idx[a:b] < kv.shape[0])).sum())
         done_tokens += b - a
@@ -208,9 +317,56 @@ def cpu_baseline(d, budget_s: float):
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"last {done_tokens} of {T} tokens ({done_keys} valid keys), numpy float64, "
+        "sample": f"last {done_tokens} of {T} tokens ({done_keys} valid keys), numpy {dtype}, "
                   f"{elapsed:.1f} s",
     }
+
+
+def host_info():
+    """CPU model, usable cores and the BLAS pool the oracle runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    blas = None
+    try:
+        import numpy as np
+        from threadpoolctl import threadpool_info
+        np.ones((64, 64)) @ np.ones((64, 64))   # loads the BLAS pool
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            blas = {"library": pools[0].get("internal_api"), "threads": pools[0].get("num_threads")}
+    except Exception:
+        pass
+    return {"cpu_model": model, "cores": cores, "blas": blas}
+
+
+def cpu_baseline_full(d, budget_s: float):
+    """The oracle as it stands: float64 on all host cores (the reported value),
+    then float32, then float64 on one BLAS thread (a per-core rate), each over
+    a bounded sample of the workload's last tokens."""
+    rec = cpu_baseline(d, budget_s)
+    rec.update(host_info())
+    rec["fp32"] = cpu_baseline(d, budget_s / 3, dtype="float32")
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            one = cpu_baseline(d, budget_s / 3)
+        one["cores"] = 1
+        rec["single_thread"] = one
+    except ImportError:
+        pass
+    rec["cores"] = rec["blas"]["threads"] if rec.get("blas") else rec["cores"]
+    return rec
 
 
 def cpu_baseline_bwd(d, dout, budget_s: float):
@@ -246,6 +402,179 @@ def cpu_baseline_bwd(d, dout, budget_s: float):
     }
 
 
+def gpu_info(dev):
+    """Device name, its maximum shader clock, and the current one as rocm-smi
+    reports it (best effort: a separate process, after the timed region)."""
+    import subprocess
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+            "sclk_max_mhz": round(getattr(p, "clock_rate", 0) / 1000) or None}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(r.stdout)
+        card = next(iter(data.values()))
+        sclk = card.get("sclk clock speed:") or card.get("sclk clock level:")
+        if sclk is not None:
+            info["sclk_now"] = sclk
+    except Exception:
+        pass
+    return info
+
+
+def time_steps(step, steps: int, warmup: int, stream):
+    """W untimed steps, then K steps, each between HIP events on `stream`.
+    Returns (average event ms, median event ms, wall ms per step)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return sum(ms) / len(ms), ms[len(ms) // 2], wall * 1e3 / steps
+
+
+def time_flushed(step, steps: int, dev, stream):
+    """Median event ms of launches that each start with no KV in L2 or the
+    MALL: a 512 MB write between launches, outside the events."""
+    import torch
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    fl = []
+    for i in range(steps):
+        scratch.fill_(i & 255)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fl.append(e0.elapsed_time(e1))
+    del scratch
+    fl.sort()
+    return fl[len(fl) // 2]
+
+
+def fwd_setup(name: str, dev, num_splits: int = 0):
+    """Inputs of a workload on the GPU and one forward step over them."""
+    import torch
+    import dsa_sparse_mla_amd as dsa
+    import workloads
+    w = workloads.WORKLOADS[name]
+    gen_dev = "cpu" if w.kind == "flat" and w.num_tokens * w.num_heads <= 2119 * 8 else "cuda"
+    d_host = workloads.make(name, device=gen_dev)
+    d = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in d_host.items()}
+    T, H = d["q"].shape[:2]
+    topk = int(d["indices"].shape[1])
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    splits, ws_bytes = dsa.workspace_size(T, H, topk, num_splits)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    if "kv" in d:
+        def step():
+            dsa.sparse_mla_fwd(d["q"], d["kv"], d["indices"], d["sm_scale"], out=out, lse=lse,
+                               num_splits=num_splits, workspace=ws)
+    else:
+        def step():
+            dsa.sparse_mla_fwd_paged(d["q"], d["kv_pages"], d["page_table"], d["seq_lens"],
+                                     d["indices"], d["sm_scale"], d["q_per_seq"], out=out, lse=lse,
+                                     num_splits=num_splits, workspace=ws)
+    return {"w": w, "d": d, "d_host": d_host if gen_dev == "cpu" else d, "T": T, "H": H, "topk": topk,
+            "splits": splits, "out": out, "lse": lse, "ws": ws, "step": step, "V": valid_keys(d)}
+
+
+def fwd_leg(name: str, dev, stream, steps: int, warmup: int, flush: bool):
+    """A second forward workload timed inside the same run: kernel time and its
+    rate against the roofline that bounds it (MFMA above 16 heads, HBM at or
+    below), warm and, with flush, with cold caches."""
+    import torch
+    f = fwd_setup(name, dev)
+    V, H = f["V"], f["H"]
+    flops = V * H * FLOP_PER_KEY_HEAD
+    gathered = V * ROW_BYTES
+    avg, med, wall = time_steps(f["step"], steps, warmup, stream)
+    rec = {"workload": f["w"].desc, "num_tokens": f["T"], "num_heads": H, "valid_keys": V,
+           "splits": f["splits"], "kernel_ms_avg": round(avg, 5), "kernel_ms_median": round(med, 5),
+           "tflops": round(flops / (avg * 1e-3) / 1e12, 2),
+           "gathered_kv_gbps": round(gathered / (avg * 1e-3) / 1e9, 1)}
+    if H > 16:
+        rec["mfma_frac"] = round(rec["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+    else:
+        rec["hbm_frac"] = round(rec["gathered_kv_gbps"] / HBM_PEAK_GBPS, 4)
+    if flush:
+        fl = time_flushed(f["step"], steps, dev, stream)
+        rec["kernel_ms_flushed"] = round(fl, 5)
+        rec["gathered_kv_gbps_flushed"] = round(gathered / (fl * 1e-3) / 1e9, 1)
+        rec["hbm_frac_flushed"] = round(rec["gathered_kv_gbps_flushed"] / HBM_PEAK_GBPS, 4)
+    t = traffic_for(name)
+    if t is not None:
+        rec["hbm_traffic_bytes"] = t
+    del f
+    torch.cuda.empty_cache()
+    return rec
+
+
+def topk_setup(name: str, dev):
+    """Index-selection inputs shaped like a workload: prefill rows select from
+    their causal prefix (their document's, when packed), decode rows from
+    their context; N(0,1) stand-in scores."""
+    import numpy as np
+    import torch
+    import workloads
+    w = workloads.WORKLOADS[name]
+    if w.kind == "paged":
+        lens = workloads.decode_lengths()
+        Q = w.extra["q_per_seq"]
+        T = lens.shape[0] * Q
+        ke = torch.tensor([int(lens[t // Q]) - Q + (t % Q) + 1 for t in range(T)], dtype=torch.int32)
+        ks = torch.zeros(T, dtype=torch.int32)
+        C = int(lens.max())
+    else:
+        T = w.num_tokens
+        cu = workloads.varlen_cu_seqlens(name) if name.startswith("varlen") else None
+        ks, ke = workloads.causal_ranges(cu, T)
+        C = T
+    scores = workloads.index_scores(T, C, seed=w.seed + 500, device=dev)
+    n = np.maximum(ke.numpy().astype(np.int64) - ks.numpy(), 0)
+    scored = int(n[n > w.topk].sum())
+    return {"w": w, "T": T, "C": C, "ks": ks.to(dev), "ke": ke.to(dev), "scores": scores, "topk": w.topk,
+            "scored": scored, "rows_scored": int((n > w.topk).sum())}
+
+
+def cpu_baseline_topk(tk, budget_s: float):
+    """Time the selection oracle on the last rows until ~budget_s."""
+    import numpy as np
+    from oracle import topk_indices_ref
+    ks, ke = tk["ks"].cpu().numpy(), tk["ke"].cpu().numpy()
+    T, k = tk["T"], tk["topk"]
+    done = rows = 0
+    elapsed = 0.0
+    t_end = T
+    while elapsed < budget_s and t_end > 0:
+        a, b = max(0, t_end - 16), t_end
+        sc = tk["scores"][a:b].cpu().numpy()
+        t0 = time.perf_counter()
+        topk_indices_ref(sc, ks[a:b], ke[a:b], k, num_cols=tk["C"])
+        elapsed += time.perf_counter() - t0
+        n = np.maximum(ke[a:b].astype(np.int64) - ks[a:b], 0)
+        done += int(n[n > k].sum())
+        rows += b - a
+        t_end = a
+    info = host_info()
+    return {"value": round(done * 4 / elapsed / 1e9, 4), "unit": "GB/s",
+            "cores": info["blas"]["threads"] if info.get("blas") else info["cores"], "kind": "oracle",
+            "sample": f"last {rows} of {T} rows ({done} scored candidates), numpy lexsort, {elapsed:.1f} s",
+            "cpu_model": info["cpu_model"]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,24 +582,38 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="swe",
                     choices=["short", "swe", "wide", "varlen16k", "varlen32k", "decode"])
-    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd"],
-                    help="fwd (the headline metric) or the backward (flat workloads)")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd", "topk"],
+                    help="fwd (the headline metric), the backward (flat workloads), or the top-k "
+                         "index selection over the workload's candidate ranges")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 skips it)")
     ap.add_argument("--flush", action="store_true",
                     help="also time launches with a 512 MB scratch write between them (caches cold), "
                          "reported as kernel_ms_flushed")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="fwd only: skip the wide-head and flushed-decode legs (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a copy of known size (for HBM counter scaling)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: store HBM bytes per launch from two counter runs")
     ap.add_argument("--traffic-command", default="",
                     help="the profiling command, recorded with --summarize-traffic")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"),
+                    help="host only: write profiles/<op>_<workload>_kernel_trace.md from a rocprofv3 "
+                         "--kernel-trace --stats run of this script (its -d directory, -o kt) and its output")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="host only: write profiles/counters_<op>_<workload>.json from rocprofv3 --pmc runs")
     args = ap.parse_args()
 
     if args.summarize_traffic:
         summarize_traffic(args.workload, *args.summarize_traffic, args.traffic_command, args.op)
+        return
+    if args.summarize_trace:
+        summarize_trace(args, *args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args, args.summarize_counters)
         return
 
     if args.gpus != 1:
@@ -281,27 +624,48 @@ def main():
     import torch
 
     import dsa_sparse_mla_amd as dsa
-    import workloads
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = workloads.WORKLOADS[args.workload]
-    gen_dev = "cpu" if w.num_tokens * w.num_heads <= 2119 * 8 else "cuda"
-    d_host = workloads.make(args.workload, device=gen_dev)
-    d = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in d_host.items()}
-    H = d["q"].shape[1]
-    T = d["q"].shape[0]
-    V = valid_keys(d)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.op == "topk":
+        tk = topk_setup(args.workload, dev)
+        idx = torch.empty((tk["T"], tk["topk"]), dtype=torch.int32, device=dev)
+
+        def step():
+            dsa.topk_indices(tk["scores"], tk["ks"], tk["ke"], tk["topk"], indices=idx)
+
+        if args.copy_calibration:
+            copy_calibration(dev)
+        avg, med, wall = time_steps(step, args.steps, args.warmup, stream)
+        moved = tk["scored"] * 4 + tk["T"] * (4 * tk["topk"] + 8)
+        gbps = moved / (wall * 1e-3) / 1e9
+        kern = moved / (avg * 1e-3) / 1e9
+        rec = {"metric": "DSA top-k index selection GB/s (scores read + index rows written, % HBM)",
+               "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+               "warmup": args.warmup, "ms_per_step": round(wall, 5), "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+               "config": {"workload": f"top-k over {tk['w'].desc} candidate ranges", "name": tk["w"].name,
+                          "op": "topk", "num_tokens": tk["T"], "num_cols": tk["C"], "topk": tk["topk"],
+                          "rows_scored": tk["rows_scored"], "scored_candidates": tk["scored"]},
+               "kernel_ms_avg": round(avg, 5), "kernel_ms_median": round(med, 5),
+               "roofline": {"bound": "hbm", "achieved": round(kern, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(kern / HBM_PEAK_GBPS, 4), "traffic": traffic_for(args.workload, "topk")},
+               "source_hash": source_hash()}
+        if args.cpu_budget > 0:
+            rec["cpu_baseline"] = cpu_baseline_topk(tk, args.cpu_budget)
+        print(json.dumps(rec), flush=True)
+        return
+
+    f = fwd_setup(args.workload, dev, args.num_splits)
+    d, T, H, V = f["d"], f["T"], f["H"], f["V"]
     gathered = V * ROW_BYTES
     flops = V * H * FLOP_PER_KEY_HEAD
-
-    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-    splits, ws_bytes = dsa.workspace_size(T, H, d["indices"].shape[1], args.num_splits)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    step = f["step"]
 
     if args.op == "bwd":
         if "kv" not in d:
@@ -309,65 +673,21 @@ def main():
             sys.exit(2)
         g = torch.Generator(device=dev).manual_seed(12345)
         dout = torch.randn((T, H, 512), generator=g, device=dev).to(torch.bfloat16)
-        dsa.sparse_mla_fwd(d["q"], d["kv"], d["indices"], d["sm_scale"], out=out, lse=lse, workspace=ws)
+        f["step"]()   # the forward supplies out and LSE
+        out, lse = f["out"], f["lse"]
         dq = torch.empty((T, H, 576), dtype=torch.float32, device=dev)
         dkv = torch.empty((d["kv"].shape[0], 576), dtype=torch.float32, device=dev)
-        bwd_schedule, bwd_ws_bytes = dsa.bwd_workspace_size(T, H, d["kv"].shape[0], d["indices"].shape[1])
+        bwd_schedule, bwd_ws_bytes = dsa.bwd_workspace_size(T, H, d["kv"].shape[0], f["topk"])
         bwd_ws = torch.empty(max(bwd_ws_bytes, 256), dtype=torch.uint8, device=dev)
 
         def step():
             dsa.sparse_mla_bwd(d["q"], d["kv"], d["indices"], d["sm_scale"], out, lse, dout,
                                dq=dq, dkv=dkv, workspace=bwd_ws)
-    elif "kv" in d:
-        def step():
-            dsa.sparse_mla_fwd(d["q"], d["kv"], d["indices"], d["sm_scale"], out=out, lse=lse,
-                               num_splits=args.num_splits, workspace=ws)
-    else:
-        def step():
-            dsa.sparse_mla_fwd_paged(d["q"], d["kv_pages"], d["page_table"], d["seq_lens"],
-                                     d["indices"], d["sm_scale"], d["q_per_seq"], out=out, lse=lse,
-                                     num_splits=args.num_splits, workspace=ws)
 
     if args.copy_calibration:
         copy_calibration(dev)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    per_launch_ms.sort()
-    avg_ms = sum(per_launch_ms) / len(per_launch_ms)
-    med_ms = per_launch_ms[len(per_launch_ms) // 2]
-    ms_per_step = wall * 1e3 / args.steps
-
-    flushed_ms = None
-    if args.flush:
-        # L2 and MALL hold no KV when each launch starts: a 512 MB write
-        # between launches, outside the events
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        fl = []
-        for i in range(args.steps):
-            scratch.fill_(i & 255)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            step()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            fl.append(e0.elapsed_time(e1))
-        fl.sort()
-        flushed_ms = fl[len(fl) // 2]
-        del scratch
+    avg_ms, med_ms, ms_per_step = time_steps(step, args.steps, args.warmup, stream)
+    flushed_ms = time_flushed(step, args.steps, dev, stream) if args.flush else None
 
     if args.op == "bwd":
         gathered = V * BWD_BYTES_PER_KEY
@@ -376,18 +696,23 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     kern_gbps = gathered / (avg_ms * 1e-3) / 1e9
     kern_tflops = flops / (avg_ms * 1e-3) / 1e12
-    bound = "hbm" if H <= 16 else "mfma"
-    if bound == "hbm":
+    traffic = traffic_for(args.workload, args.op)
+    if H <= 16:
         roof = {"bound": "hbm", "achieved": round(kern_gbps, 2), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(kern_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_for(args.workload)}
+                "unit": "GB/s", "frac": round(kern_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
+        if traffic is not None:
+            # the counters' bytes beyond the L2 over the same launch time: at or
+            # near the gathered rate only when the rows really come from HBM
+            roof["traffic_gbps"] = round(traffic / (avg_ms * 1e-3) / 1e9, 1)
+            roof["traffic_frac"] = round(roof["traffic_gbps"] / HBM_PEAK_GBPS, 4)
+            if traffic < 0.25 * gathered:
+                roof["served_from"] = ("L2/MALL: the gathered rows are cache-resident (counter traffic is "
+                                       f"{100 * traffic / gathered:.1f}% of the gathered bytes); "
+                                       "decode_flushed is the HBM-bound case")
     else:
         roof = {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_for(args.workload)}
+                "unit": "TFLOP/s", "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
 
-    if args.op == "bwd":
-        roof["traffic"] = traffic_for(args.workload, "bwd")
     rec = {
         "metric": METRIC if args.op == "fwd" else BWD_METRIC,
         "value": round(gbps, 2),
@@ -401,9 +726,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.desc, "name": w.name, "num_tokens": T, "num_heads": H,
-                   "topk": int(d["indices"].shape[1]), "dqk": 576, "dv": 512,
-                   "valid_keys": V, "splits": splits},
+        "config": {"workload": f["w"].desc, "name": f["w"].name, "num_tokens": T, "num_heads": H,
+                   "topk": f["topk"], "dqk": 576, "dv": 512, "valid_keys": V, "splits": f["splits"]},
         "tflops": round(tflops, 3),
         "gathered_kv_gbps": round(gbps, 2),
         "kernel_ms_avg": round(avg_ms, 5),
@@ -420,11 +744,21 @@ def main():
         rec["config"]["op"] = "bwd"
         rec["config"]["schedule"] = bwd_schedule
         rec["bytes_per_key"] = BWD_BYTES_PER_KEY
+    cpu_src = f["d_host"]
+    del f
+    if args.op == "fwd" and not args.no_legs and args.workload == "swe":
+        # the other half of the metric (TFLOP/s at 64 heads) and the HBM-bound
+        # 8-head case with cold caches, measured in the same run
+        legs_steps = max(3, min(args.steps, 10))
+        torch.cuda.empty_cache()
+        rec["wide"] = fwd_leg("wide", dev, stream, legs_steps, 2, flush=False)
+        rec["decode_flushed"] = fwd_leg("decode", dev, stream, legs_steps, 2, flush=True)
+    rec["gpu"] = gpu_info(dev)
     if args.cpu_budget > 0:
         if args.op == "bwd":
-            rec["cpu_baseline"] = cpu_baseline_bwd(d_host if gen_dev == "cpu" else d, dout, args.cpu_budget)
+            rec["cpu_baseline"] = cpu_baseline_bwd(cpu_src, dout, args.cpu_budget)
         else:
-            rec["cpu_baseline"] = cpu_baseline(d_host if gen_dev == "cpu" else d, args.cpu_budget)
+            rec["cpu_baseline"] = cpu_baseline_full(cpu_src, args.cpu_budget)
     print(json.dumps(rec), flush=True)
 
 

@@ -85,3 +85,55 @@ def test_flop_and_byte_constants():
     assert bench.BWD_FLOP_PER_KEY_HEAD == 2 * (3 * 576 + 2 * 512)
     assert bench.BWD_BYTES_PER_KEY == 1152
     assert np.isclose(bench.HBM_PEAK_GBPS, 8000.0) and np.isclose(bench.MFMA_BF16_PEAK_TFLOPS, 2500.0)
+
+
+def test_trace_summary(tmp_path):
+    """The kernel-trace summary is written from a rocprofv3 trace directory and
+    the script's own JSON line, with the command that made it."""
+    import argparse
+    d = tmp_path / "kt"
+    d.mkdir()
+    with open(d / "kt_kernel_stats.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"])
+        w.writeheader()
+        w.writerow({"Name": "void dsa::topk_select_kernel(dsa::TopkArgs)", "Calls": 4, "AverageNs": 50000,
+                    "MinNs": 49000, "MaxNs": 51000, "Percentage": 90.0})
+    with open(d / "kt_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for i, dur in enumerate((60000, 49000, 50000, 51000)):
+            w.writerow({"Kernel_Name": "void dsa::topk_select_kernel(dsa::TopkArgs)",
+                        "Start_Timestamp": 10 ** 9 * i, "End_Timestamp": 10 ** 9 * i + dur})
+    log = tmp_path / "b.log"
+    rec = {"steps": 3, "warmup": 1, "source_hash": "x", "config": {"workload": "w"}, "kernel_ms_avg": 0.05,
+           "ms_per_step": 0.06, "roofline": {"bound": "hbm", "achieved": 1, "unit": "GB/s", "peak": 8000, "frac": 0.1}}
+    log.write_text("noise\n" + json.dumps(rec) + "\n")
+    args = argparse.Namespace(op="topk", workload="wide")
+    bench.summarize_trace(args, str(d), str(log), out_dir=str(tmp_path))
+    text = (tmp_path / "dsa_topk_wide_kernel_trace.md").read_text()
+    assert "--op topk --workload wide --steps 3 --warmup 1" in text
+    assert "50.0 us average over the last 3 launches" in text     # the warm-up launch is left out
+
+
+def test_counter_summary(tmp_path):
+    """Counters per dispatch of the op's kernel only; MFMA-busy fraction
+    against GRBM_GUI_ACTIVE x 1024 SIMDs, L2 hit fraction from TCC hits and misses."""
+    import argparse
+    p = tmp_path / "pmc.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for disp in (1, 2, 3):
+            k = "void dsa::sparse_mla_fwd_ws_kernel<false>(dsa::FwdArgs)"
+            w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES",
+                        "Counter_Value": 512000})
+            w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "GRBM_GUI_ACTIVE",
+                        "Counter_Value": 1000})
+            w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "TCC_HIT_sum", "Counter_Value": 75})
+            w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "TCC_MISS_sum", "Counter_Value": 25})
+        w.writerow({"Dispatch_Id": 9, "Kernel_Name": "at::neg", "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": 5})
+    args = argparse.Namespace(op="fwd", workload="wide", traffic_command="cmd")
+    bench.summarize_counters(args, [str(p)], out_dir=str(tmp_path))
+    out = json.load(open(tmp_path / "counters_fwd_wide.json"))
+    assert out["mfma_busy_frac"] == 0.5 and out["l2_hit_frac"] == 0.75
+    assert out["dispatches"]["GRBM_GUI_ACTIVE"] == 3
