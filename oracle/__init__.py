@@ -13,3 +13,4 @@ from .sparse_mla_ref import (  # noqa: F401
 )
 from .bwd_ref import sparse_mla_bwd_ref  # noqa: F401,E402
 from .topk_ref import topk_indices_ref  # noqa: F401,E402
+from .fp8_cache_ref import dequantize_rows, e4m3_to_float, sparse_mla_fwd_paged_fp8_ref  # noqa: F401,E402

@@ -285,3 +285,37 @@ def index_scores(num_tokens: int, num_cols: int, seed: int, device="cpu", kind="
     elif kind != "normal":
         raise KeyError(kind)
     return s
+
+
+# ---------------------------------------------------------------- FP8 MLA cache
+
+FP8_ROW_BYTES = 656   # 512 e4m3 latent values, 4 fp32 group scales, 64 bf16 rope values
+
+
+def quantize_fp8_rows(kv: torch.Tensor) -> torch.Tensor:
+    """bf16 rows [..., 576] -> FP8 MLA cache rows uint8 [..., 656], as a cache
+    writer would store them: each group of 128 latent values gets the scale
+    max|x| / 448 (fp32; 1 for an all-zero group) and its values x / scale
+    rounded to e4m3; the 64 rope values are kept in bf16."""
+    lead = kv.shape[:-1]
+    lat = kv[..., :512].float().reshape(*lead, 4, 128)
+    amax = lat.abs().amax(dim=-1, keepdim=True)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    codes = (lat / scale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    out = torch.empty((*lead, FP8_ROW_BYTES), dtype=torch.uint8, device=kv.device)
+    out[..., :512] = codes.reshape(*lead, 512)
+    out[..., 512:528] = scale.reshape(*lead, 4).contiguous().view(torch.uint8)
+    out[..., 528:] = kv[..., 512:].contiguous().view(torch.uint8)
+    return out
+
+
+def make_paged_fp8(device="cpu", **kw):
+    """The paged-decode inputs (make_paged, same seeds and sizes) with the
+    cache stored as FP8 MLA rows: kv_pages becomes uint8 [P, page_size, 656]."""
+    d = make_paged(device=device, **kw)
+    pages = d["kv_pages"]
+    fp8 = torch.empty((*pages.shape[:-1], FP8_ROW_BYTES), dtype=torch.uint8, device=pages.device)
+    for p0 in range(0, pages.shape[0], 1024):
+        fp8[p0:p0 + 1024] = quantize_fp8_rows(pages[p0:p0 + 1024])
+    d["kv_pages"] = fp8
+    return d
