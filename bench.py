@@ -39,6 +39,7 @@ HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "sparse MLA fwd TFLOP/s + gathered-KV GB/s (% roofline), topk=2048, dqk576/dv512"
 ROW_BYTES = 576 * 2
+FP8_ROW_BYTES = 656   # an FP8 MLA cache row: 512 e4m3 + 4 fp32 scales + 64 bf16
 FLOP_PER_KEY_HEAD = 2 * (576 + 512)
 # backward: QK^T (576), dO V^T (512), dQ (576), dK (576), dV (512) per key and head
 BWD_METRIC = "sparse MLA bwd TFLOP/s + gathered-KV GB/s (% roofline), topk=2048, dqk576/dv512"
@@ -271,12 +272,16 @@ def valid_keys(d) -> int:
 def cpu_baseline(d, budget_s: float, dtype="float64"):
     """Time the CPU oracle on the last tokens of the workload until ~budget_s."""
     import numpy as np
-    from oracle import sparse_mla_fwd_paged_ref, sparse_mla_fwd_ref
+    from oracle import sparse_mla_fwd_paged_fp8_ref, sparse_mla_fwd_paged_ref, sparse_mla_fwd_ref
+    import torch
     q = d["q"].float().cpu().numpy()
     idx = d["indices"].cpu().numpy()
     paged = "kv_pages" in d
+    fp8 = paged and d["kv_pages"].dtype == torch.uint8
+    row_bytes = FP8_ROW_BYTES if fp8 else ROW_BYTES
     if paged:
-        kvp = d["kv_pages"].float().cpu().numpy()
+        # FP8 rows stay raw (the oracle dequantises the pages a chunk uses)
+        kvp = d["kv_pages"].cpu().numpy() if fp8 else d["kv_pages"].float().cpu().numpy()
         table = d["page_table"].cpu().numpy()
         lens = d["seq_lens"].cpu().numpy()
         Q = d["q_per_seq"]
@@ -295,8 +300,18 @@ def cpu_baseline(d, budget_s: float, dtype="float64"):
             s0 = max(0, s1 - max(1, chunk // Q))
             a, b = s0 * Q, s1 * Q
             t0 = time.perf_counter()
-            sparse_mla_fwd_paged_ref(q[a:b], kvp, table[s0:s1], lens[s0:s1], idx[a:b],
-                                     d["sm_scale"], Q, dtype=getattr(np, dtype))
+            if fp8:
+                # only this chunk's pages, renumbered
+                tab = table[s0:s1]
+                used = np.unique(tab[tab >= 0])
+                remap = np.full(kvp.shape[0], -1, dtype=np.int64)
+                remap[used] = np.arange(used.size)
+                small = np.where(tab >= 0, remap[np.maximum(tab, 0)], -1).astype(np.int32)
+                sparse_mla_fwd_paged_fp8_ref(q[a:b], kvp[used], small, lens[s0:s1], idx[a:b],
+                                             d["sm_scale"], Q, dtype=getattr(np, dtype))
+            else:
+                sparse_mla_fwd_paged_ref(q[a:b], kvp, table[s0:s1], lens[s0:s1], idx[a:b],
+                                         d["sm_scale"], Q, dtype=getattr(np, dtype))
             elapsed += time.perf_counter() - t0
             seq = np.arange(a, b) // Q - s0
             done_keys += int(((idx[a:b] >= 0) & (idx[a:b] < lens[s0:s1][seq][:, None])).sum())
@@ -313,7 +328,7 @@ def cpu_baseline(d, budget_s: float, dtype="float64"):
     except AttributeError:
         cores = os.cpu_count()
     return {
-        "value": round(done_keys * ROW_BYTES / elapsed / 1e9, 4),
+        "value": round(done_keys * row_bytes / elapsed / 1e9, 4),
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
@@ -470,6 +485,7 @@ def fwd_setup(name: str, dev, num_splits: int = 0):
     import workloads
     w = workloads.WORKLOADS[name]
     gen_dev = "cpu" if w.kind == "flat" and w.num_tokens * w.num_heads <= 2119 * 8 else "cuda"
+    fp8 = w.kind == "paged_fp8"
     d_host = workloads.make(name, device=gen_dev)
     d = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in d_host.items()}
     T, H = d["q"].shape[:2]
@@ -483,11 +499,12 @@ def fwd_setup(name: str, dev, num_splits: int = 0):
             dsa.sparse_mla_fwd(d["q"], d["kv"], d["indices"], d["sm_scale"], out=out, lse=lse,
                                num_splits=num_splits, workspace=ws)
     else:
+        fwd = dsa.sparse_mla_fwd_paged_fp8 if fp8 else dsa.sparse_mla_fwd_paged
+
         def step():
-            dsa.sparse_mla_fwd_paged(d["q"], d["kv_pages"], d["page_table"], d["seq_lens"],
-                                     d["indices"], d["sm_scale"], d["q_per_seq"], out=out, lse=lse,
-                                     num_splits=num_splits, workspace=ws)
-    return {"w": w, "d": d, "d_host": d_host if gen_dev == "cpu" else d, "T": T, "H": H, "topk": topk,
+            fwd(d["q"], d["kv_pages"], d["page_table"], d["seq_lens"], d["indices"], d["sm_scale"],
+                d["q_per_seq"], out=out, lse=lse, num_splits=num_splits, workspace=ws)
+    return {"row_bytes": FP8_ROW_BYTES if fp8 else ROW_BYTES, "w": w, "d": d, "d_host": d_host if gen_dev == "cpu" else d, "T": T, "H": H, "topk": topk,
             "splits": splits, "out": out, "lse": lse, "ws": ws, "step": step, "V": valid_keys(d)}
 
 
@@ -499,7 +516,7 @@ def fwd_leg(name: str, dev, stream, steps: int, warmup: int, flush: bool):
     f = fwd_setup(name, dev)
     V, H = f["V"], f["H"]
     flops = V * H * FLOP_PER_KEY_HEAD
-    gathered = V * ROW_BYTES
+    gathered = V * f["row_bytes"]
     avg, med, wall = time_steps(f["step"], steps, warmup, stream)
     rec = {"workload": f["w"].desc, "num_tokens": f["T"], "num_heads": H, "valid_keys": V,
            "splits": f["splits"], "kernel_ms_avg": round(avg, 5), "kernel_ms_median": round(med, 5),
@@ -581,7 +598,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="swe",
-                    choices=["short", "swe", "wide", "varlen16k", "varlen32k", "decode"])
+                    choices=["short", "swe", "wide", "varlen16k", "varlen32k", "decode", "decode_fp8"])
     ap.add_argument("--op", default="fwd", choices=["fwd", "bwd", "topk"],
                     help="fwd (the headline metric), the backward (flat workloads), or the top-k "
                          "index selection over the workload's candidate ranges")
@@ -663,7 +680,7 @@ def main():
 
     f = fwd_setup(args.workload, dev, args.num_splits)
     d, T, H, V = f["d"], f["T"], f["H"], f["V"]
-    gathered = V * ROW_BYTES
+    gathered = V * f["row_bytes"]
     flops = V * H * FLOP_PER_KEY_HEAD
     step = f["step"]
 
@@ -753,6 +770,7 @@ def main():
         torch.cuda.empty_cache()
         rec["wide"] = fwd_leg("wide", dev, stream, legs_steps, 2, flush=False)
         rec["decode_flushed"] = fwd_leg("decode", dev, stream, legs_steps, 2, flush=True)
+        rec["decode_fp8_flushed"] = fwd_leg("decode_fp8", dev, stream, legs_steps, 2, flush=True)
     rec["gpu"] = gpu_info(dev)
     if args.cpu_budget > 0:
         if args.op == "bwd":

@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     sparse_mla_bwd,
     sparse_mla_fwd,
     sparse_mla_fwd_paged,
+    sparse_mla_fwd_paged_fp8,
     sparse_mla_fwd_paged_noalloc,
     topk_indices,
     workspace_size,

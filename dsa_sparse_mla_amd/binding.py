@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
             vp, i64,                 # lse
             i32, vp, i64,            # num_splits, workspace, bytes
             vp]                      # stream
+        L.dsa_sparse_mla_fwd_paged_fp8.restype = ctypes.c_int
+        L.dsa_sparse_mla_fwd_paged_fp8.argtypes = L.dsa_sparse_mla_fwd_paged.argtypes
         L.dsa_sparse_mla_fwd_paged_noalloc.restype = ctypes.c_int
         # the paged arguments up to num_splits, without workspace/bytes
         L.dsa_sparse_mla_fwd_paged_noalloc.argtypes = L.dsa_sparse_mla_fwd_paged.argtypes[:-3] + [
@@ -238,6 +240,50 @@ def sparse_mla_fwd_paged(q, kv_pages, page_table, seq_lens, indices, sm_scale, q
             stream)
     if st != 0:
         raise DsaError(st, "dsa_sparse_mla_fwd_paged")
+    return out, lse
+
+
+FP8_ROW_BYTES = 656
+
+
+def sparse_mla_fwd_paged_fp8(q, kv_pages, page_table, seq_lens, indices, sm_scale, q_per_seq,
+                             out=None, lse=None, num_splits=0, workspace=None):
+    """Sparse MLA forward over a paged FP8 MLA cache (decode), no gather copy.
+
+    kv_pages: uint8 [P, page_size, >= 656] FP8 MLA rows (512 e4m3 latent values
+    in 4 groups of 128, 4 fp32 scales, 64 bf16 rope values); the other
+    arguments as in sparse_mla_fwd_paged (at most 32 heads).
+    """
+    dev = q.device
+    _check(q, "q", torch.bfloat16, 3, dev)
+    _check(kv_pages, "kv_pages", torch.uint8, 3, dev)
+    _check(page_table, "page_table", torch.int32, 2, dev)
+    _check(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _check(indices, "indices", torch.int32, 2, dev)
+    T, H, D = q.shape
+    S = page_table.shape[0]
+    if D != DQK or kv_pages.shape[2] < FP8_ROW_BYTES:
+        raise ValueError("q rows must be 576 wide and FP8 cache rows at least 656 bytes")
+    if seq_lens.shape[0] != S or T != S * q_per_seq or indices.shape[0] != T:
+        raise ValueError("need num_seqs * q_per_seq query tokens and one seq_len per sequence")
+    topk = indices.shape[1]
+    out, lse = _outputs(q, T, H, out, lse)
+    ws, ws_bytes = _workspace(q, T, H, topk, num_splits, workspace)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib().dsa_sparse_mla_fwd_paged_fp8(
+            q.data_ptr(), q.stride(0), q.stride(1),
+            kv_pages.data_ptr(), kv_pages.stride(0), kv_pages.stride(1),
+            kv_pages.shape[0], kv_pages.shape[1],
+            page_table.data_ptr(), page_table.stride(0), page_table.shape[1], seq_lens.data_ptr(),
+            indices.data_ptr(), indices.stride(0),
+            S, int(q_per_seq), H, topk, float(sm_scale),
+            out.data_ptr(), out.stride(0), out.stride(1),
+            lse.data_ptr(), lse.stride(0),
+            int(num_splits), ws.data_ptr() if ws is not None else None, ws_bytes,
+            stream)
+    if st != 0:
+        raise DsaError(st, "dsa_sparse_mla_fwd_paged_fp8")
     return out, lse
 
 

@@ -209,8 +209,9 @@ void bwd_plan(int64_t T, int32_t H, int64_t N, int32_t topk, BwdPlan* p) {
 }
 
 // Heads per workgroup: 16, 32 or 64 (HT head tiles of 16); more heads use
-// several workgroups per token, one per block of 64.
-template <bool PAGED>
+// several workgroups per token, one per block of 64. FP8 (paged FP8 cache):
+// blocks of up to 32 heads only.
+template <bool PAGED, bool FP8 = false>
 int launch(dsa::FwdArgs& args, hipStream_t stream) {
   const int H = args.num_heads;
   const int ht = head_tiles(H);
@@ -218,9 +219,11 @@ int launch(dsa::FwdArgs& args, hipStream_t stream) {
   const dim3 grid((unsigned)(args.num_tokens * args.splits * args.head_blocks));
   const dim3 block(64 * dsa::kWaves);
   if (ht == 1) {
-    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<1, PAGED>), grid, block, 0, stream, args);
+    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<1, PAGED, FP8>), grid, block, 0, stream, args);
   } else if (ht == 2) {
-    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<2, PAGED>), grid, block, 0, stream, args);
+    hipLaunchKernelGGL((dsa::sparse_mla_fwd_kernel<2, PAGED, FP8>), grid, block, 0, stream, args);
+  } else if (FP8) {
+    return DSA_ERR_UNSUPPORTED;
   } else {
     hipLaunchKernelGGL((dsa::sparse_mla_fwd_ws_kernel<PAGED>), grid, dim3(64 * dsa::kWsWaves), 0, stream, args);
   }
@@ -394,6 +397,74 @@ int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stri
   st = device_check();
   if (st != DSA_OK) return st;
   return launch<true>(a, static_cast<hipStream_t>(stream));
+}
+
+int dsa_sparse_mla_fwd_paged_fp8(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                                 const void* kv_pages, int64_t kv_stride_page_bytes, int64_t kv_stride_row_bytes,
+                                 int64_t num_pages, int32_t page_size, const int32_t* page_table,
+                                 int64_t page_table_stride, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                 const int32_t* indices, int64_t idx_stride_tok, int32_t num_seqs,
+                                 int32_t q_per_seq, int32_t num_heads, int32_t topk, float sm_scale, void* out,
+                                 int64_t out_stride_tok, int64_t out_stride_head, float* lse,
+                                 int64_t lse_stride_tok, int32_t num_splits, void* workspace,
+                                 int64_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || q_per_seq < 1) return DSA_ERR_INVALID_ARGUMENT;
+  const int64_t T = (int64_t)num_seqs * q_per_seq;
+  int st = check_common(q, q_stride_tok, q_stride_head, indices, idx_stride_tok, T, num_heads, topk, out,
+                        out_stride_tok, out_stride_head, lse, lse_stride_tok);
+  if (st != DSA_OK || T == 0) return st;
+  if (num_heads > 32) return DSA_ERR_UNSUPPORTED;   // the FP8 path runs blocks of up to 32 heads
+  if (page_size < 1 || page_size > 4096 || (page_size & (page_size - 1))) return DSA_ERR_UNSUPPORTED;
+  if (num_pages < 0 || max_pages_per_seq < 0 || page_table_stride < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (!seq_lens || !aligned(seq_lens, 4)) return DSA_ERR_INVALID_ARGUMENT;
+  if (max_pages_per_seq > 0 && (!page_table || !aligned(page_table, 4))) return DSA_ERR_INVALID_ARGUMENT;
+  if (num_seqs > 1 && max_pages_per_seq > 0 && page_table_stride < max_pages_per_seq)
+    return DSA_ERR_INVALID_ARGUMENT;
+  if (num_pages > 0) {
+    if (!kv_pages || !aligned(kv_pages, 16) || kv_stride_row_bytes % 16 || kv_stride_page_bytes % 16)
+      return DSA_ERR_INVALID_ARGUMENT;
+    if ((page_size > 1 && kv_stride_row_bytes < DSA_FP8_ROW_BYTES) ||
+        (num_pages > 1 && kv_stride_page_bytes < (int64_t)page_size * kv_stride_row_bytes))
+      return DSA_ERR_INVALID_ARGUMENT;
+    const int64_t span = (num_pages - 1) * (kv_stride_page_bytes / 16) + (int64_t)page_size * (kv_stride_row_bytes / 16);
+    if (span >= ((int64_t)1 << 32)) return DSA_ERR_UNSUPPORTED;
+  }
+  dsa::FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  st = fill_outputs_and_splits(a, q, q_stride_tok, q_stride_head, indices, idx_stride_tok, T, num_heads, topk,
+                               sm_scale, out, out_stride_tok, out_stride_head, lse, lse_stride_tok, num_splits,
+                               workspace, workspace_bytes);
+  if (st != DSA_OK) return st;
+  a.kv = static_cast<const uint8_t*>(kv_pages);
+  a.kv_row_gran = kv_stride_row_bytes / 16;
+  a.kv_page_gran = kv_stride_page_bytes / 16;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  a.page_shift = shift;
+  a.page_mask = page_size - 1;
+  a.page_table = page_table;
+  a.pt_stride = page_table_stride;
+  a.max_pages = max_pages_per_seq;
+  a.seq_lens = seq_lens;
+  a.q_per_seq = q_per_seq;
+  a.num_pages = num_pages;
+  {
+    int64_t ws_need = 0;
+    int sp = 0, sl = 0;
+    check_splits(T, num_heads, topk, num_splits, &sp, &sl, &ws_need);
+    const int64_t rows = num_pages > 0 ? ((num_pages - 1) * kv_stride_page_bytes + (int64_t)page_size * kv_stride_row_bytes) : 0;
+    st = check_overlaps(
+        {extent3(out, T, out_stride_tok, num_heads, out_stride_head, DSA_DV, 2),
+         extent2(lse, T, lse_stride_tok, num_heads, 4), extent2(ws_need > 0 ? workspace : nullptr, 1, 0, ws_need, 1)},
+        {extent3(q, T, q_stride_tok, num_heads, q_stride_head, DSA_DQK, 2), extent2(kv_pages, 1, 0, rows, 1),
+         extent2(indices, T, idx_stride_tok, topk, 4),
+         extent2(page_table, num_seqs, page_table_stride, max_pages_per_seq, 4),
+         extent2(seq_lens, 1, 0, num_seqs, 4)});
+    if (st != DSA_OK) return st;
+  }
+  st = device_check();
+  if (st != DSA_OK) return st;
+  return launch<true, true>(a, static_cast<hipStream_t>(stream));
 }
 
 int dsa_sparse_mla_fwd_paged_noalloc(const void* q, int64_t q_stride_tok, int64_t q_stride_head,

@@ -285,7 +285,55 @@ __device__ __forceinline__ void issue_tile(const FwdArgs& a, const uint32_t* s_g
   dma_16b(a.kv + ((uint64_t)gr + 64u + (uint32_t)g) * 16ull, base + kRopeOff + wave * 1024);
 }
 
-template <int HT, bool PAGED>
+// FP8 MLA cache rows (paged decode over an FP8 cache): 656 bytes per key,
+// 512 float8 e4m3 latent values in 4 groups of 128, then 4 fp32 scales (one
+// per group), then the 64 rope values in bf16. A tile is brought in by every
+// wave for rows 8w .. 8w+7: lane i reads row 8w + i/8, latent granules
+// (i & 7) + 8g of group g (16 codes each), the row's 4 scales and rope
+// granule i & 7 -- six 16-byte loads into registers, two steps ahead.
+constexpr int kFp8Scales = 512;   // byte offset of the scales in a row
+constexpr int kFp8Rope = 528;     // byte offset of the rope values
+struct Fp8Share {
+  uint4 v[6];   // latent granules of groups 0..3, the scales, the rope granule
+};
+
+__device__ __forceinline__ void fp8_load(const FwdArgs& a, const uint32_t* s_goff, int t, int wave, int lane,
+                                         Fp8Share& b) {
+  const int r = 8 * wave + (lane >> 3);
+  const uint8_t* row = a.kv + (uint64_t)s_goff[t * kTileKeys + r] * 16ull;
+  const int g = lane & 7;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) b.v[q] = *(const uint4*)(row + 16 * (g + 8 * q));
+  b.v[4] = *(const uint4*)(row + kFp8Scales);
+  b.v[5] = *(const uint4*)(row + kFp8Rope + 16 * g);
+}
+
+// Dequantise this wave's share of a tile into its LDS stage, in the layout
+// the bf16 gather produces: e4m3 -> fp32 (v_cvt_pk_f32_fp8, exact), times
+// the group's fp32 scale, rounded to bf16; the rope granule as it is.
+__device__ __forceinline__ void fp8_store(uint8_t* stage, int wave, int lane, const Fp8Share& b) {
+  const int r = 8 * wave + (lane >> 3);
+  const int g = lane & 7;
+  const float4_t sc = __builtin_bit_cast(float4_t, b.v[4]);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w[4] = {b.v[q].x, b.v[q].y, b.v[q].z, b.v[q].w};
+    uint32_t o[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);   // codes 4k, 4k+1
+      const float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);    // codes 4k+2, 4k+3
+      o[2 * k] = pack_bf16x2(lo[0] * sc[q], lo[1] * sc[q]);
+      o[2 * k + 1] = pack_bf16x2(hi[0] * sc[q], hi[1] * sc[q]);
+    }
+    const int G = 2 * (g + 8 * q);   // logical 16-byte granule of the first 8 values
+    *(uint4*)(stage + r * 1024 + 16 * (G ^ swz(r))) = (uint4){o[0], o[1], o[2], o[3]};
+    *(uint4*)(stage + r * 1024 + 16 * ((G + 1) ^ swz(r))) = (uint4){o[4], o[5], o[6], o[7]};
+  }
+  *(uint4*)(stage + kRopeOff + r * 128 + 16 * (g ^ ((r >> 1) & 7))) = b.v[5];
+}
+
+template <int HT, bool PAGED, bool FP8 = false>
 __global__ void __launch_bounds__(256)
 sparse_mla_fwd_kernel(const FwdArgs a) {
   using S = FwdShape<HT>;
@@ -467,7 +515,22 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
     }
   };
 
-  auto step = [&](const uint8_t* st_s, bool do_s, int jn, const uint8_t* st_pv, bool do_pv, int issue_j) {
+  // FP8: the share of the tile that a step dequantises (f8_cur) and the one
+  // still in flight (f8_nxt); the caller alternates them
+  Fp8Share f8a, f8b;
+  // The step's gather: the bf16 path issues the copies of tile issue_j; the
+  // FP8 path dequantises tile issue_j (loaded two steps ago) into its stage
+  // and loads tile issue_j + 2 into the same registers.
+  auto gather = [&](int issue_j, Fp8Share& f8) {
+    if constexpr (FP8) {
+      fp8_store(s_stage + (issue_j % kStages) * kStageBytes, wave, lane, f8);
+      if (issue_j + 2 < ntiles) fp8_load(a, s_goff, issue_j + 2, wave, lane, f8);
+    } else {
+      issue_tile(a, s_goff, stage_lds, issue_j, wave, lane);
+    }
+  };
+  auto step = [&](const uint8_t* st_s, bool do_s, int jn, const uint8_t* st_pv, bool do_pv, int issue_j,
+                  Fp8Share& f8) {
     constexpr int kS = S::kSSteps;        // 36 QK^T MFMAs: (chunk t/2, block t%2)
     constexpr int kP = S::kDvTiles;       // PV MFMAs: value tile u
     constexpr int kPA = kP / 2;           // PV MFMAs placed in phase A
@@ -493,7 +556,7 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
         sacc[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[t % (kKA + 1)], qreg[t >> 1], sacc[t & 1], 0, 0, 0);
         if (t >= kS - 2) asm volatile("" : "+v"(sacc[t & 1]));   // scores in VGPRs: read by the softmax
         if (do_pv && (t & 1) && (t >> 1) < kPA) pv_mfma(t >> 1);
-        if (t == 3 && issue_j >= 0) issue_tile(a, s_goff, stage_lds, issue_j, wave, lane);
+        if (t == 3 && issue_j >= 0) gather(issue_j, f8);
         __builtin_amdgcn_sched_barrier(0);
       }
       // phase B: remaining PV MFMAs with softmax slices (slot 0 left free so
@@ -511,7 +574,7 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
 #pragma unroll
       for (int u = 0; u < kP; ++u) {
         pv_mfma(u);
-        if (u == 1 && issue_j >= 0) issue_tile(a, s_goff, stage_lds, issue_j, wave, lane);
+        if (u == 1 && issue_j >= 0) gather(issue_j, f8);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -538,7 +601,7 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
 
   auto stage_ptr = [&](int j) { return (const uint8_t*)s_stage + (j % kStages) * kStageBytes; };
 
-  if (ntiles > 0) {
+  if (ntiles > 0 && !FP8) {
     // prologue: tiles 0..2 in flight, then QK^T and softmax of tile 0
     issue_tile(a, s_goff, stage_lds, 0, wave, lane);
     if (ntiles > 1) issue_tile(a, s_goff, stage_lds, 1, wave, lane);
@@ -547,16 +610,41 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
     else if (ntiles > 1) wait_vmem<kDmaPerWave>();
     else wait_vmem<0>();
     __syncthreads();
-    step(stage_ptr(0), true, 0, stage_ptr(0), false, -1);
+    step(stage_ptr(0), true, 0, stage_ptr(0), false, -1, f8a);
     // steady state: PV of tile j with QK^T and softmax of tile j+1
     for (int j = 0; j + 1 < ntiles; ++j) {
       if (j + 2 < ntiles) wait_vmem<kDmaPerWave>();   // tile j+1 landed; tile j+2 may still fly
       else wait_vmem<0>();
       __syncthreads();   // ... in every wave; and tile j-1's stage is free for tile j+3
-      step(stage_ptr(j + 1), true, j + 1, stage_ptr(j), true, j + 3 < ntiles ? j + 3 : -1);
+      step(stage_ptr(j + 1), true, j + 1, stage_ptr(j), true, j + 3 < ntiles ? j + 3 : -1, f8a);
     }
     // PV of the last tile
-    step(stage_ptr(ntiles - 1), false, ntiles - 1, stage_ptr(ntiles - 1), true, -1);
+    step(stage_ptr(ntiles - 1), false, ntiles - 1, stage_ptr(ntiles - 1), true, -1, f8a);
+  }
+  if (ntiles > 0 && FP8) {
+    // prologue: tiles 0 and 1 dequantised into their stages, tiles 2 and 3
+    // in flight (tile t in f8a if t is even, f8b if odd)
+    fp8_load(a, s_goff, 0, wave, lane, f8a);
+    if (ntiles > 1) fp8_load(a, s_goff, 1, wave, lane, f8b);
+    fp8_store(s_stage, wave, lane, f8a);
+    if (ntiles > 2) fp8_load(a, s_goff, 2, wave, lane, f8a);
+    if (ntiles > 1) fp8_store(s_stage + kStageBytes, wave, lane, f8b);
+    if (ntiles > 3) fp8_load(a, s_goff, 3, wave, lane, f8b);
+    __syncthreads();
+    step(stage_ptr(0), true, 0, stage_ptr(0), false, -1, f8a);
+    // steady state: PV of tile j, QK^T and softmax of tile j+1, tile j+2
+    // dequantised into the stage tile j-2 left (its loads landed a step ago),
+    // tile j+4 loaded; two steps per pass so each share stays in its registers
+    int j = 0;
+    while (j + 1 < ntiles) {
+      __syncthreads();   // tile j+1 stored in every wave; tile j-2's stage is free
+      step(stage_ptr(j + 1), true, j + 1, stage_ptr(j), true, j + 2 < ntiles ? j + 2 : -1, f8a);
+      if (++j + 1 >= ntiles) break;
+      __syncthreads();
+      step(stage_ptr(j + 1), true, j + 1, stage_ptr(j), true, j + 2 < ntiles ? j + 2 : -1, f8b);
+      ++j;
+    }
+    step(stage_ptr(ntiles - 1), false, ntiles - 1, stage_ptr(ntiles - 1), true, -1, f8a);
   }
 
   // ---------------------------------------------------------------- 6. epilogue

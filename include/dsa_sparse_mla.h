@@ -156,6 +156,46 @@ int dsa_sparse_mla_fwd_paged(const void* q, int64_t q_stride_tok, int64_t q_stri
                              void* stream);
 
 /*
+ * Sparse MLA forward over a paged FP8 MLA KV cache (decode), with no gather
+ * copy: the rows are dequantised on the way into the kernel's LDS tiles.
+ * Pages: "feat: add XTuner TileLang sparse MLA backend" (lmdeploy PR 4904),
+ * Summary (that backend rejects the FP8 MLA KV-cache path) and per-file
+ * overview (BF16 and FP8 sparse decode behaviour; the DeepSeek-V3.2
+ * configuration defaults the DSA MLA cache to BF16 with an FP8 policy
+ * possible elsewhere). The pages do not lay out an FP8 row; the layout taken
+ * here is the published DeepSeek-V3.2 sparse-attention FP8 cache row:
+ *
+ *   bytes   0 .. 511  512 latent values, float8 e4m3 (OCP: bias 7, no
+ *                     infinities, S.1111.111 is NaN), in 4 groups of 128;
+ *   bytes 512 .. 527  4 float32 scales, one per group;
+ *   bytes 528 .. 655  64 rope values, bfloat16.
+ *
+ * A key's row is latent[g*128 + i] = e4m3 * scale[g], rope as stored; the
+ * result is the BF16 paged forward on those rows, except that each latent
+ * value is rounded to bf16 (round to nearest even) after the scaling, as the
+ * kernel's MFMA operands are bf16.
+ *
+ * kv_pages   uint8 [num_pages, page_size, >= 656]: row r of page p at byte
+ *            p*kv_stride_page_bytes + r*kv_stride_row_bytes (16-byte aligned,
+ *            strides multiples of 16).
+ * Other arguments, limits and results as in dsa_sparse_mla_fwd_paged, with
+ * num_heads <= 32 (DSA_ERR_UNSUPPORTED above).
+ */
+#define DSA_FP8_ROW_BYTES 656
+int dsa_sparse_mla_fwd_paged_fp8(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                                 const void* kv_pages, int64_t kv_stride_page_bytes,
+                                 int64_t kv_stride_row_bytes, int64_t num_pages, int32_t page_size,
+                                 const int32_t* page_table, int64_t page_table_stride,
+                                 int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                 const int32_t* indices, int64_t idx_stride_tok,
+                                 int32_t num_seqs, int32_t q_per_seq, int32_t num_heads,
+                                 int32_t topk, float sm_scale,
+                                 void* out, int64_t out_stride_tok, int64_t out_stride_head,
+                                 float* lse, int64_t lse_stride_tok,
+                                 int32_t num_splits, void* workspace, int64_t workspace_bytes,
+                                 void* stream);
+
+/*
  * dsa_sparse_mla_fwd_paged without a workspace argument, for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, and harnesses that forbid allocation. The split partials go to a

@@ -21,6 +21,8 @@ packing):
             64, pages a random permutation), 6 query tokens per sequence
             (1 + 5 speculative), 8 heads; row (b, j) = topk distinct logical
             positions of the causal context of query j
+  decode_fp8  the same inputs with the cache stored as FP8 MLA rows (656
+            bytes: e4m3 latent values with a scale per 128, bf16 rope)
 
 Values: Q and KV are N(0,1) in fp32 from torch.Generator(seed), rounded to
 bf16. Index structure comes from numpy.random.default_rng(seed). The softmax
@@ -66,6 +68,11 @@ WORKLOADS = {
                        "paged bf16 decode, 64 seqs x 6 query tokens, 8 heads",
                        {"num_seqs": 64, "q_per_seq": 6, "page_size": 64,
                         "min_len": 4096, "max_len": 65536}),
+    # the decode workload with its cache stored as FP8 MLA rows (same seeds)
+    "decode_fp8": Workload("decode_fp8", "paged_fp8", 64 * 6, 8, TOPK, 5,
+                           "paged FP8-cache decode, 64 seqs x 6 query tokens, 8 heads",
+                           {"num_seqs": 64, "q_per_seq": 6, "page_size": 64,
+                            "min_len": 4096, "max_len": 65536}),
 }
 
 
@@ -242,6 +249,8 @@ def make(name: str, device="cpu", **kw):
     """Inputs of any named workload (see the module docstring)."""
     if WORKLOADS[name].kind == "paged":
         return make_paged(device=device, **kw)
+    if WORKLOADS[name].kind == "paged_fp8":
+        return make_paged_fp8(device=device, **kw)
     return make_flat(name, device=device, **kw)
 
 
