@@ -12,7 +12,10 @@ import threading
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_sparse_mla.so")
+# DSA_SPARSE_MLA_LIB names another build of the same library (for example a
+# host-sanitizer build); by default the one built next to this file.
+LIB_PATH = os.environ.get("DSA_SPARSE_MLA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                                "libdsa_sparse_mla.so")
 DQK = 576
 DV = 512
 
