@@ -122,7 +122,7 @@ def workspace_size(num_tokens: int, num_heads: int, topk: int, num_splits: int =
     return s.value, b.value
 
 
-BWD_SCHEDULES = {0: "token-major", 1: "kv-major"}
+BWD_SCHEDULES = {0: "token-major", 1: "kv-major", 2: "split"}
 
 
 def bwd_workspace_size(num_tokens: int, num_heads: int, num_kv: int, topk: int):

@@ -63,7 +63,8 @@ struct BwdArgs {
   float* dkv;              // fp32 [N, 576], zeroed before this kernel
   int64_t dkv_st;
   int32_t head_blocks;     // workgroups per token (16 heads each)
-  const uint32_t* only;    // if set, tokens with only[t] == 0 are skipped (done by the kv-major pass)
+  const uint32_t* only;    // if set, tokens are filtered by only[t] (see only_nonzero)
+  int32_t only_nonzero;    // 1: run the tokens with only[t] != 0; 0: those with only[t] == 0
 };
 
 constexpr int kBwPitch = 1168;                  // LDS row pitch of K rows and Q rows: 1152 + 16
@@ -80,7 +81,8 @@ __device__ __forceinline__ bf16x8_t join4(short4_t lo, short4_t hi) {
 // HT head tiles of 16 per workgroup (1 or 2). With 2, each key's dkv row is
 // added once per 32 heads instead of once per 16, and each tile is gathered
 // once for 32 heads.
-template <int HT>
+// DKV = false compiles the dkv phase out: the dq pass of the split schedule.
+template <int HT, bool DKV = true>
 __global__ void __launch_bounds__(256)
 sparse_mla_bwd_kernel(const BwdArgs a) {
   constexpr int HB = 16 * HT;   // heads of the workgroup
@@ -100,7 +102,7 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
   const int n = lane & 15, g = lane >> 4;   // MFMA column / k-group of the lane
   const int64_t token = blockIdx.x / a.head_blocks;
   const int h0 = (int)(blockIdx.x % a.head_blocks) * HB;
-  if (a.only && a.only[token] == 0) return;   // uniform over the workgroup
+  if (a.only && ((a.only[token] != 0u) != (a.only_nonzero != 0))) return;   // uniform over the workgroup
 
   // ---------------------------------------------------------------- per-token inputs
   // Q (HB x 576) and dO (HB x 512) of the head block into LDS; padded heads are 0.
@@ -263,7 +265,7 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
       }
       // ---- phase 3b: dkv of key block kb2 = w >> 1, column tiles 18(w & 1) .. +17:
       //   [16 keys x 16 columns] = (s dS)^T Q + P^T dO over the HB heads
-      {
+      if constexpr (DKV) {
         const int kb2 = wave >> 1;
         const int kbase = j * kTileKeys + kb2 * 16 + 4 * g;   // this lane's outputs: keys kbase + e
         uint32_t rid[4];
@@ -358,8 +360,10 @@ constexpr int kKvMaxWords = 8192;   // mask words per token row held in LDS (kv 
 struct KvMajorArgs {
   uint32_t* mask;     // u32 [num_words][num_tokens]: word w of token t at mask[w * T + t]
   uint32_t* dup;      // u32 [num_tokens]: 1 = the row names a kv row twice
-  float* dbuf;        // fp32 [num_tokens][16]: D = dO . O per head (0 past num_heads)
+  float* dbuf;        // fp32 [num_tokens][d_st]: D = dO . O per head (0 past num_heads)
+  int64_t d_st;       // heads per token row of dbuf: 16, or num_heads above 16
   int32_t num_words;  // ceil(num_kv / 32)
+  int32_t zero_dq;    // 1: the prepass zeroes dq (the kv-major pass adds into it)
 };
 
 __global__ void __launch_bounds__(256)
@@ -379,9 +383,8 @@ sparse_mla_bwd_prep_kernel(const BwdArgs a, const KvMajorArgs m) {
       if (atomicOr(&s_bm[v >> 5], bit) & bit) s_dup = 1u;
     }
   }
-  // D per head (wave w: heads 4w .. 4w+3) and dq = 0 for this token
-  for (int hh = 0; hh < 4; ++hh) {
-    const int h = 4 * wave + hh;
+  // D per head (wave w: heads w, w + 4, ..) and, for the kv-major pass, dq = 0
+  for (int h = wave; h < m.d_st; h += 4) {
     float d = 0.f;
     if (h < a.num_heads) {
       const bf16x8_t o = *(const bf16x8_t*)(a.out + token * a.o_st + (int64_t)h * a.o_sh + 8 * lane);
@@ -391,10 +394,11 @@ sparse_mla_bwd_prep_kernel(const BwdArgs a, const KvMajorArgs m) {
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) d += __shfl_xor(d, off);
-    if (lane == 0) m.dbuf[token * 16 + h] = d;
+    if (lane == 0) m.dbuf[token * m.d_st + h] = d;
   }
-  for (int i = tid; i < a.num_heads * kDqk; i += 256)
-    a.dq[token * a.dq_st + (int64_t)(i / kDqk) * a.dq_sh + i % kDqk] = 0.f;
+  if (m.zero_dq)
+    for (int i = tid; i < a.num_heads * kDqk; i += 256)
+      a.dq[token * a.dq_st + (int64_t)(i / kDqk) * a.dq_sh + i % kDqk] = 0.f;
   __syncthreads();
   const uint32_t dup = s_dup;
   if (tid == 0) m.dup[token] = dup;
@@ -481,6 +485,7 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
   const uint16_t* const do_ptr = a.dout;
   const float* const lse_ptr = a.lse;
   const float* const dbuf = m.dbuf;
+  const int64_t d_st = m.d_st;
   float* const dq_ptr = a.dq;
   const int64_t q_st = a.q_st, q_sh = a.q_sh, do_st = a.do_st, do_sh = a.do_sh, lse_st = a.lse_st;
   const int64_t dq_st = a.dq_st, dq_sh = a.dq_sh;
@@ -518,7 +523,7 @@ sparse_mla_bwd_kv_kernel(const BwdArgs a, const KvMajorArgs m) {
       pok = ti < np && hh < num_heads;
       const int64_t t = t0 + s_tok[ti < np ? ti : np - 1];
       pl2 = *(pok ? lse_ptr + t * lse_st + hh : lse_ptr);   // scaled when stored: no wait on the loads here
-      pD = *(pok ? dbuf + t * 16 + hh : dbuf);
+      pD = *(pok ? dbuf + t * d_st + hh : dbuf);
     }
   };
   auto store_step = [&](int buf) {

@@ -16,6 +16,7 @@
 #include "fwd_kernel.hpp"
 #include "fwd_kernel_ws.hpp"
 #include "bwd_kernel.hpp"
+#include "bwd_kvw_kernel.hpp"
 #include "topk_kernel.hpp"
 
 namespace {
@@ -192,15 +193,19 @@ void bwd_plan(int64_t T, int32_t H, int64_t N, int32_t topk, BwdPlan* p) {
   *p = BwdPlan();
   if (T <= 0 || N <= 0) return;
   const int64_t words = (N + 31) / 32;
-  const int64_t chunks = (T + dsa::kKvChunk - 1) / dsa::kKvChunk;
+  const bool wide = H > 16;
+  const int64_t chunks = (T + (wide ? dsa::kKwChunk : dsa::kKvChunk) - 1) / (wide ? dsa::kKwChunk : dsa::kKvChunk);
   const int64_t mask_bytes = words * T * 4;
   const int64_t dup_off = round_up(mask_bytes, 256);
   const int64_t d_off = dup_off + round_up(T * 4, 256);
-  const int64_t bytes = d_off + T * 16 * 4;
-  const bool kv_major = H <= 16 && words <= dsa::kKvMaxWords && 3 * N * H <= 256 * (int64_t)topk &&
-                        bytes <= ((int64_t)1 << 30) && words * chunks < ((int64_t)1 << 31);
-  if (!kv_major) return;
-  p->schedule = DSA_BWD_KV_MAJOR;
+  const int64_t bytes = d_off + T * (wide ? H : 16) * 4;
+  // kv-major (H <= 16) and split (H > 16) need rows that name a large share
+  // of the kv rows; both keep the prepass bitmap in LDS and the grid in 31 bits
+  const bool dense = wide ? N <= 16 * (int64_t)topk : 3 * N * H <= 256 * (int64_t)topk;
+  const bool fits = words <= dsa::kKvMaxWords && bytes <= ((int64_t)1 << 30) &&
+                    (words + 1) / 2 * chunks < ((int64_t)1 << 31);
+  if (!dense || !fits) return;
+  p->schedule = wide ? DSA_BWD_SPLIT : DSA_BWD_KV_MAJOR;
   p->words = words;
   p->chunks = chunks;
   p->dup_off = dup_off;
@@ -580,17 +585,33 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
   const int64_t wgs = num_tokens * a.head_blocks;
   if (wgs >= ((int64_t)1 << 31)) return DSA_ERR_UNSUPPORTED;
 
-  if (plan.schedule == DSA_BWD_KV_MAJOR) {
+  if (plan.schedule != DSA_BWD_TOKEN_MAJOR) {
+    const bool split = plan.schedule == DSA_BWD_SPLIT;
     dsa::KvMajorArgs m;
     m.mask = static_cast<uint32_t*>(workspace);
     m.dup = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + plan.dup_off);
     m.dbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.d_off);
+    m.d_st = split ? num_heads : 16;
     m.num_words = (int32_t)plan.words;
+    m.zero_dq = split ? 0 : 1;
+    const dim3 kv_grid((unsigned)((plan.words + 1) / 2 * plan.chunks));
     hipLaunchKernelGGL(dsa::sparse_mla_bwd_prep_kernel, dim3((unsigned)num_tokens), dim3(256), 0, s, a, m);
-    hipLaunchKernelGGL(dsa::sparse_mla_bwd_kv_kernel, dim3((unsigned)((plan.words + 1) / 2 * plan.chunks)),
-                       dim3(256), 0, s, a, m);
-    a.only = m.dup;   // rows with a repeated entry: token-major
-    hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, s, a);
+    if (split) {
+      // dkv of every token whose row repeats no entry, then dq of those
+      // tokens; the tokens with a repeated entry take the full token-major
+      // kernel (dq, and dkv with atomics)
+      hipLaunchKernelGGL(dsa::sparse_mla_bwd_kvw_kernel, kv_grid, dim3(256), 0, s, a, m);
+      a.only = m.dup;
+      a.only_nonzero = 0;
+      hipLaunchKernelGGL((dsa::sparse_mla_bwd_kernel<2, false>), dim3((unsigned)wgs), dim3(256), 0, s, a);
+      a.only_nonzero = 1;
+      hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(dsa::sparse_mla_bwd_kv_kernel, kv_grid, dim3(256), 0, s, a, m);
+      a.only = m.dup;   // rows with a repeated entry: token-major
+      a.only_nonzero = 1;
+      hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, s, a);
+    }
   } else if (hb == 16) {
     hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, s, a);
   } else {

@@ -251,19 +251,24 @@ int dsa_sparse_mla_fwd_paged_noalloc(const void* q, int64_t q_stride_tok, int64_
  * dq       fp32 [num_tokens, num_heads, 576] (written); element (t,h,d) at
  *          dq + t*dq_stride_tok + h*dq_stride_head + d.
  * dkv      fp32 [num_kv, 576] (written: zeroed, then accumulated with atomic
- *          adds, so the order of additions into a row is not fixed and two
- *          calls may differ in the last bits); row i at dkv + i*dkv_stride_row.
+ *          adds of partial sums, so the order of additions into a row is not
+ *          fixed and two calls may differ in the last bits); row i at
+ *          dkv + i*dkv_stride_row.
  *          16-byte aligned, dkv_stride_row a multiple of 4 and >= 576.
  * stream   hipStream_t to enqueue on.
  *
- * Two schedules, chosen from the sizes alone (dsa_sparse_mla_bwd_workspace_size
+ * Three schedules, chosen from the sizes alone (dsa_sparse_mla_bwd_workspace_size
  * reports which one a call takes). Token-major: one workgroup per token and
  * head block adds each named row's gradient into dkv; it needs no workspace.
- * kv-major, when num_heads <= 16, 0 < num_kv <= 262144 and 3 * num_kv *
- * num_heads <= 256 * topk (rows that name a large share of kv, as in causal
- * prefill), and its workspace is at most 1 GiB: one workgroup per (64 kv
- * rows, 64-token chunk) keeps the rows' dkv in registers and adds dq with
- * atomics instead, so dq too may then differ in the last bits between calls.
+ * The other two serve rows that name a large share of kv (as in causal
+ * prefill), when 0 < num_kv <= 262144 and their workspace is at most 1 GiB:
+ *   kv-major (num_heads <= 16 and 3 * num_kv * num_heads <= 256 * topk): one
+ *     workgroup per (64 kv rows, 64-token chunk) keeps the rows' dkv in
+ *     registers and adds dq with atomics instead, so dq too may then differ
+ *     in the last bits between calls;
+ *   split (num_heads > 16 and num_kv <= 16 * topk): a kv-major pass per
+ *     (64 kv rows, 256-token chunk) computes dkv, and a token-major pass
+ *     computes and writes dq (no atomics on dq).
  * Tokens whose row names some kv row twice go to the token-major kernel
  * within the same call.
  * workspace/workspace_bytes  device scratch owned by the caller, at least the
@@ -292,6 +297,7 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
 /* Backward schedules reported by dsa_sparse_mla_bwd_workspace_size. */
 #define DSA_BWD_TOKEN_MAJOR 0
 #define DSA_BWD_KV_MAJOR 1
+#define DSA_BWD_SPLIT 2
 
 /*
  * Workspace query for dsa_sparse_mla_bwd. The pages that motivate it: the
@@ -300,8 +306,9 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
  * workspace its kernel required; here the caller learns the size up front.
  *
  * num_tokens, num_heads, num_kv, topk: as in the backward call.
- * *schedule_out (may be NULL): DSA_BWD_TOKEN_MAJOR or DSA_BWD_KV_MAJOR, the
- *   schedule a backward call with these sizes takes (on any device).
+ * *schedule_out (may be NULL): DSA_BWD_TOKEN_MAJOR, DSA_BWD_KV_MAJOR or
+ *   DSA_BWD_SPLIT, the schedule a backward call with these sizes takes (on
+ *   any device).
  * *bytes_out: workspace bytes that call needs (0 for the token-major schedule).
  * Returns DSA_OK, DSA_ERR_INVALID_ARGUMENT (negative sizes, NULL bytes_out) or
  * DSA_ERR_UNSUPPORTED (num_heads or topk out of range).

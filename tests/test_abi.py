@@ -226,9 +226,12 @@ def test_valid_call_reaches_the_device_check():
     # out right after q (adjacent, not overlapping) passes the overlap check too
     assert _fwd(out=fake(0) + 2 * 8 * 8 * 576) in (HIPERR, UNSUPPORTED)
     assert _bwd(ws=fake(8), ws_bytes=1 << 20) in (HIPERR, UNSUPPORTED)
-    # token-major sizes (64 heads) take no workspace
-    assert _bwd(H=64, q_st=64 * 576, o_st=64 * 512, lse_st=64, do_st=64 * 512,
-                dq_st=64 * 576) in (HIPERR, UNSUPPORTED)
+    # split sizes (64 heads, 100 kv rows) need a workspace; sparse rows at 64
+    # heads (40000 kv rows > 16 x topk) take the token-major kernel and none
+    wide = dict(H=64, q_st=64 * 576, o_st=64 * 512, lse_st=64, do_st=64 * 512, dq_st=64 * 576)
+    assert _bwd(**wide) == WORKSPACE
+    assert _bwd(ws=fake(8), ws_bytes=1 << 20, **wide) in (HIPERR, UNSUPPORTED)
+    assert _bwd(num_kv=40000, **wide) in (HIPERR, UNSUPPORTED)
 
 
 def _bwd_ws(T, H, N, topk):
@@ -242,8 +245,10 @@ def _round256(x):
 @pytest.mark.parametrize("T,H,N,topk,schedule", [
     (2119, 8, 2119, 2048, "kv-major"),        # SWE-like prefill rows
     (150, 16, 200, 160, "kv-major"),
-    (150, 17, 200, 160, "token-major"),        # more than 16 heads
-    (8192, 64, 8192, 2048, "token-major"),
+    (150, 17, 200, 160, "split"),              # more than 16 heads
+    (8192, 64, 8192, 2048, "split"),           # wide-head causal prefill
+    (32768, 64, 32768, 2048, "split"),         # num_kv = 16 topk
+    (32768, 64, 32769, 2048, "token-major"),   # sparser rows
     (100, 8, 5000, 64, "token-major"),         # sparse rows: 3 N H > 256 topk
     (3, 1, 262144, 3072, "kv-major"),          # 3 N H = 256 topk, the whole LDS bitmap
     (3, 1, 262145, 3072, "token-major"),       # one row more than the bitmap holds
@@ -251,13 +256,14 @@ def _round256(x):
     (10, 8, 0, 2048, "token-major"),           # no kv rows
 ])
 def test_bwd_workspace_query(T, H, N, topk, schedule):
-    """The schedule comes from the sizes alone, and the kv-major workspace is
-    the occupancy masks, the repeat flags and D, each 256-byte aligned."""
+    """The schedule comes from the sizes alone, and the kv-major and split
+    workspaces are the occupancy masks, the repeat flags and D (16 heads per
+    token, or all of them above 16), each 256-byte aligned."""
     got, nbytes = _bwd_ws(T, H, N, topk)
     assert got == schedule
-    if schedule == "kv-major":
+    if schedule != "token-major":
         words = (N + 31) // 32
-        assert nbytes == _round256(words * T * 4) + _round256(T * 4) + T * 64
+        assert nbytes == _round256(words * T * 4) + _round256(T * 4) + T * max(H, 16) * 4
     else:
         assert nbytes == 0
 
@@ -267,6 +273,8 @@ def test_bwd_workspace_cap():
     T, N = 65536, 131072   # 4096 words x 65536 tokens x 4 bytes = 1 GiB of masks alone
     assert _bwd_ws(T, 1, N, 65536)[0] == "token-major"
     assert _bwd_ws(T // 2, 1, N, 65536)[0] == "kv-major"
+    assert _bwd_ws(T, 64, N, 65536)[0] == "token-major"
+    assert _bwd_ws(T // 2, 64, N, 65536)[0] == "split"
 
 
 def test_bwd_workspace_query_rejects_bad_sizes():

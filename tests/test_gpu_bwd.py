@@ -254,14 +254,20 @@ def test_bwd_kv_major_causal_rows():
 
 
 def test_bwd_paths_of_the_cases():
-    """The cases above reach both kernels: the token-major one above 16 heads
-    and for sparse rows (5000 kv rows, topk up to 64, 8 heads), the kv-major
-    pass for the SWE-like rows and the small dense cases."""
+    """The cases above reach every schedule: the token-major kernel for sparse
+    rows (5000 kv rows, topk up to 64), the kv-major pass for the SWE-like
+    rows and the small dense cases at up to 16 heads, the split schedule
+    above 16 heads."""
     assert not kv_major(8, 5000, 64) and not kv_major(8, 5000, 1) and kv_major(8, 5000, 2049)
     assert kv_major(8, 300, 100) and kv_major(16, 300, 100) and not kv_major(17, 300, 100)
     d = workloads.make_flat("swe")
     assert kv_major(d["q"].shape[1], d["kv"].shape[0], d["indices"].shape[1])
     assert not kv_major(64, 300, 100)
+    # above 16 heads: the split schedule for the small cases, the wide and
+    # packed workloads; the token-major kernel for rows sparser than that
+    assert split(17, 300, 100) and split(48, 300, 100) and split(64, 300, 100) and split(128, 500, 150)
+    assert split(64, 8192, 2048, 8192) and split(64, 16384, 2048, 16384) and split(64, 32768, 2048, 32768)
+    assert not split(64, 5000, 64) and not split(16, 300, 100)
 
 
 @pytest.mark.parametrize("N", [262144, 262145])
@@ -338,3 +344,115 @@ def test_bwd_kv_major_long_causal_rows():
     rdq, rdkv = ref(d["q"], d["kv"], d["indices"], d["sm_scale"], dout)
     check_grad(np64(dq), rdq, "dq long causal kv-major")
     check_grad(np64(dkv), rdkv, "dkv long causal kv-major")
+
+
+def split(H, N, topk, T=64):
+    """The split schedule (more than 16 heads and num_kv <= 16 topk), as the
+    library's workspace query reports it."""
+    return _dsa().bwd_workspace_size(T, H, N, topk)[0] == "split"
+
+
+@pytest.mark.parametrize("H", [17, 32, 33, 64, 128])
+def test_bwd_split_schedule(H):
+    """The split schedule: 300 tokens (two 256-token chunks of the dkv pass,
+    the last ragged), 200 kv rows (four 64-row blocks, the last with 8 rows),
+    distinct entries with -1 and out-of-range values; a token with no key, a
+    token with only out-of-range values, and two tokens that name a row twice
+    (those two take the full token-major kernel inside the same call). Head
+    counts that fill one or several 32-head groups, and ones that pad them."""
+    T, N, topk = 300, 200, 160
+    assert split(H, N, topk)
+    q, kv, idx, dout = random_case(T, H, N, topk, seed=400 + H, dup=False)
+    idx[4] = -1
+    idx[9] = 213
+    idx[40, 0] = idx[40, 1] = 17           # duplicate pair
+    idx[290, 5] = idx[290, 100] = 199      # duplicate of the last row
+    dq, dkv = run(q, kv, idx, 1 / 24, dout)
+    dq, dkv = np64(dq), np64(dkv)
+    assert np.all(dq[4] == 0) and np.all(dq[9] == 0)
+    named = set(int(v) for v in idx.numpy().ravel() if 0 <= v < N)
+    untouched = [r for r in range(N) if r not in named]
+    assert np.all(dkv[untouched] == 0)
+    rdq, rdkv = ref(q, kv, idx, 1 / 24, dout)
+    check_grad(dq, rdq, f"dq split H={H}")
+    check_grad(dkv, rdkv, f"dkv split H={H}")
+
+
+def test_bwd_split_causal_rows():
+    """Causal rows at 64 heads (token t names min(t + 1, 256) of its keys 0..t,
+    tail padding): blocks named by every later token, by a quarter of them,
+    and at the diagonal by one token."""
+    d = workloads.make_flat("wide", num_tokens=520, topk=256)
+    T, H = d["q"].shape[:2]
+    assert split(H, d["kv"].shape[0], 256)
+    g = torch.Generator().manual_seed(14)
+    dout = torch.randn((T, H, 512), generator=g).to(torch.bfloat16)
+    dq, dkv = run(d["q"], d["kv"], d["indices"], d["sm_scale"], dout)
+    rdq, rdkv = ref(d["q"], d["kv"], d["indices"], d["sm_scale"], dout)
+    check_grad(np64(dq), rdq, "dq causal split")
+    check_grad(np64(dkv), rdkv, "dkv causal split")
+
+
+def test_bwd_split_strided():
+    """The split schedule on strided views: q every other head of a wider
+    tensor, kv rows 640 apart, index rows with trailing columns, dO a head
+    slice, dq and dkv views into larger buffers that stay untouched outside
+    the views; 40 heads (a full and a padded head group)."""
+    T, H, N, k = 100, 40, 150, 120
+    assert split(H, N, k)
+    q_big, kv, idx, dout_big = random_case(T, 2 * H, N, k, seed=32, dup=False)
+    q = q_big[:, ::2]
+    dout = dout_big[:, 3:3 + H]
+    kv_big = torch.zeros((N, 640), dtype=torch.bfloat16)
+    kv_big[:, :576] = kv
+    idx_big = torch.full((T, k + 8), 7, dtype=torch.int32)
+    idx_big[:, :k] = idx
+    dsa = _dsa()
+    qd = q_big.to(DEV)[:, ::2]
+    dod = dout_big.to(DEV)[:, 3:3 + H]
+    kvd = kv_big.to(DEV)[:, :576]
+    idd = idx_big.to(DEV)[:, :k]
+    o, l = sparse_mla_fwd_ref(np64(q), np64(kv), idx.numpy(), 1 / 24)
+    out = torch.from_numpy(o).to(torch.bfloat16).to(DEV)
+    lse = torch.from_numpy(l).float().to(DEV)
+    dq_big = torch.full((T, H, 640), 7.0, device=DEV)
+    dkv_big = torch.full((N, 600), 7.0, device=DEV)
+    dq, dkv = dsa.sparse_mla_bwd(qd, kvd, idd, 1 / 24, out, lse, dod,
+                                 dq=dq_big[:, :, :576], dkv=dkv_big[:, :576])
+    torch.cuda.synchronize()
+    assert (dq_big[:, :, 576:] == 7.0).all() and (dkv_big[:, 576:] == 7.0).all()
+    rdq, rdkv = ref(q, kv, idx, 1 / 24, dout)
+    check_grad(np64(dq), rdq, "dq strided split")
+    check_grad(np64(dkv), rdkv, "dkv strided split")
+
+
+def test_bwd_wide_full_sampled():
+    """The wide-head prefill at full size (8192 tokens, 64 heads, topk 2048,
+    the split schedule), in the configuration bench.py --op bwd times, on
+    outputs the oracle can compute one by one: dq of sampled tokens (a
+    token's dq depends on its own row only) and dkv of sampled kv rows (a
+    row's dkv is complete once every token that names it is included).
+    out and LSE of those tokens are the oracle's; the other tokens' (which
+    reach none of the sampled outputs) are the library's forward."""
+    dsa = _dsa()
+    d = workloads.make_flat("wide", device=DEV)
+    T, H = d["q"].shape[:2]
+    N = d["kv"].shape[0]
+    assert split(H, N, 2048, T)
+    dout = workloads.randn_bf16((T, H, 512), 77, DEV)
+    idx = d["indices"].cpu().numpy()
+    rows = np.array([8000, 8063, 8064, 8100, 8150, 8191])
+    toks = np.array([0, 1, 2047, 2048, 4095, 6000, 8191])
+    naming = np.flatnonzero(np.isin(idx, rows).any(axis=1))
+    U = np.union1d(naming, toks)
+    q_u, kv_c = np64(d["q"][torch.from_numpy(U).to(DEV)]), np64(d["kv"])
+    o_u, l_u = sparse_mla_fwd_ref(q_u, kv_c, idx[U], d["sm_scale"])
+    out, lse = dsa.sparse_mla_fwd(d["q"], d["kv"], d["indices"], d["sm_scale"])
+    ut = torch.from_numpy(U).to(DEV)
+    out[ut] = torch.from_numpy(o_u).to(torch.bfloat16).to(DEV)
+    lse[ut] = torch.from_numpy(l_u).float().to(DEV)
+    dq, dkv = dsa.sparse_mla_bwd(d["q"], d["kv"], d["indices"], d["sm_scale"], out, lse, dout)
+    torch.cuda.synchronize()
+    rdq, rdkv = sparse_mla_bwd_ref(q_u, kv_c, idx[U], d["sm_scale"], np64(dout[ut]))
+    check_grad(np64(dq[ut]), rdq, "dq wide sampled tokens")
+    check_grad(np64(dkv[torch.from_numpy(rows).to(DEV)]), rdkv[rows], "dkv wide sampled rows")
