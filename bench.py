@@ -221,8 +221,13 @@ def summarize_trace(args, trace_dir: str, log_path: str, out_dir: str | None = N
 def summarize_counters(args, csv_paths, out_dir: str | None = None):
     """Median per dispatch of every counter in rocprofv3 --pmc CSVs, for the
     op's kernel, into profiles/counters_<op>_<workload>.json, with derived
-    MFMA-busy and L2 hit fractions. SQ_VALU_MFMA_BUSY_CYCLES is compared with
-    GRBM_GUI_ACTIVE (the dispatch's GPU cycles) x 1024 SIMDs."""
+    MFMA-busy, L2 hit and LDS bank-conflict fractions.
+
+    SQ counters are summed over the shader engines, so a dispatch's cycles
+    are SQ_BUSY_CYCLES / Num_Shader_Banks (32 on MI355X), and the MFMA-busy
+    fraction is SQ_VALU_MFMA_BUSY_CYCLES / (Simd_Count x those cycles), both
+    counts from the run's pmc_agent_info.csv (defaults 1024 SIMDs, 32
+    engines)."""
     import csv
     import statistics
     kern = OP_KERNEL[args.op]
@@ -241,14 +246,29 @@ def summarize_counters(args, csv_paths, out_dir: str | None = None):
     if not per:
         raise SystemExit("no dispatch of the op's kernel in the counter files")
     med = {c: statistics.median(v.values()) for c, v in per.items()}
+    simds, engines = 1024, 32
+    for path in csv_paths:
+        info = os.path.join(os.path.dirname(path), "pmc_agent_info.csv")
+        if os.path.exists(info):
+            with open(info) as f:
+                for row in csv.DictReader(f):
+                    if row.get("Agent_Type", "").upper().endswith("GPU") or "gfx" in row.get("Name", ""):
+                        simds = int(row.get("Simd_Count") or simds)
+                        engines = int(row.get("Num_Shader_Banks") or engines)
+                        break
+            break
     out = {"workload": args.workload, "op": args.op, "source_hash": source_hash(),
            "kernels": sorted(names), "dispatches": {c: len(v) for c, v in per.items()}, "counters": med,
-           "command": args.traffic_command}
-    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and med.get("GRBM_GUI_ACTIVE"):
-        out["mfma_busy_frac"] = round(med["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024.0 * med["GRBM_GUI_ACTIVE"]), 4)
+           "simds": simds, "shader_engines": engines, "command": args.traffic_command}
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and med.get("SQ_BUSY_CYCLES"):
+        cycles = med["SQ_BUSY_CYCLES"] / engines
+        out["cycles_per_dispatch"] = cycles
+        out["mfma_busy_frac"] = round(med["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cycles), 4)
     hit, miss = med.get("TCC_HIT_sum"), med.get("TCC_MISS_sum")
     if hit is not None and miss is not None and hit + miss > 0:
         out["l2_hit_frac"] = round(hit / (hit + miss), 4)
+    if med.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in med:
+        out["lds_conflict_frac"] = round(med["SQ_LDS_BANK_CONFLICT"] / med["SQ_LDS_IDX_ACTIVE"], 4)
     path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"counters_{args.op}_{args.workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)

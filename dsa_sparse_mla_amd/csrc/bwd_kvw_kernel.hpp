@@ -92,6 +92,7 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
   __shared__ int s_tok[kKwChunk];
   __shared__ uint64_t s_msk[kKwChunk];
   __shared__ int s_wcnt[4];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[4][4096];   // the wave pairs' exchange area
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -137,118 +138,157 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
   const int64_t d_st = m.d_st;
   const float scale = a.scale, scale_log2 = a.scale_log2;
 
-  // ---- the wave's K rows as B operands: lane (g, n) holds row 16w + n, columns 32c + 8g .. +7
-  bf16x8_t kreg[kDqk / 32];
-  {
-    const int64_t row = r0 + 16 * wave + n;
+  // Waves pair up: wave (rh, ch) = (w >> 1, w & 1) owns rows r0 + 32rh ..
+  // +31 (two row tiles) and half ch of the columns: latent 256ch .. +255
+  // and rope 32ch .. +31 (nine 32-column chunks) for S^T, the latent half
+  // for dP^T, and the same 288 columns of dkv. Each q / dO operand read
+  // then feeds two MFMAs (one per row tile).
+  const int rh = wave >> 1, ch = wave & 1;
+
+  // ---- K rows as B operands: kreg[rt][j], lane (g, n) holds row 32rh + 16rt + n,
+  // columns 32 chunk(j) + 8g .. +7 (chunk j < 8: latent 8ch + j; j = 8: rope half ch)
+  bf16x8_t kreg[2][9];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int64_t row = r0 + 32 * rh + 16 * rt + n;
     const bool ok = row < a.num_kv;
     const uint16_t* src = a.kv + (ok ? row : 0) * a.kv_st + 8 * g;
 #pragma unroll
-    for (int c = 0; c < kDqk / 32; ++c) {
-      const bf16x8_t v = *(const bf16x8_t*)(src + 32 * c);
-      kreg[c] = ok ? v : (bf16x8_t){};
+    for (int j = 0; j < 9; ++j) {
+      const bf16x8_t v = *(const bf16x8_t*)(src + (j < 8 ? 32 * (8 * ch + j) : kDv + 32 * ch));
+      kreg[rt][j] = ok ? v : (bf16x8_t){};
     }
   }
 
   // ---- copies of step s into buffer b: 17 one-KB copies per wave (q latent
   // rows wave + 4k, dO rows wave + 4k, q rope rows 8w .. 8w+7), and wave 0
-  // copies LSE and D
-  auto issue = [&](int s, int b) {
-    const int p = s / groups, hg = s - p * groups;
-    const int64_t tok = t0 + s_tok[p];
-    const int h0 = kKwHeads * hg;
-    const uint32_t bb = lds_offset(&s_buf[b][0]);
-    const uint16_t* qt = q_ptr + tok * q_st;
-    const uint16_t* dt = do_ptr + tok * do_st;
+  // copies LSE and D. A plan holds the step's scalar bases; copy(k) issues
+  // copy k (k < 8: q row, k < 16: dO row, 16: rope rows, 17: LSE/D), so that
+  // the copies can be spread over the MFMA stream. The latent and dO copies
+  // take a scalar base per head row and a fixed lane offset (row h = wave +
+  // 4k has the swizzle of h & 15 = wave + 4 (k & 3)); padded heads copy the
+  // group's last head.
+  uint32_t cp_off[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int h = wave + 4 * k;
-      const int hq = min(h0 + h, num_heads - 1);
-      dma_16b(qt + hq * q_sh + 8 * (lane ^ kw_swz(h)), bb + kKwQL + h * 1024);
-      dma_16b(dt + hq * do_sh + 8 * (lane ^ kw_swz(h)), bb + kKwDO + h * 1024);
-    }
-    {
+  for (int j = 0; j < 4; ++j) cp_off[j] = 16u * (uint32_t)(lane ^ kw_swz(wave + 4 * j));
+  const int64_t q_sh2 = 2 * q_sh, do_sh2 = 2 * do_sh;   // bytes
+  struct CopyPlan {
+    uint64_t qb, db;       // byte addresses of the step's token, head h0
+    const uint16_t* qt;    // the token's q row
+    int64_t tok;
+    int h0, hmax;
+    uint32_t bb;           // LDS byte address of the target buffer
+  };
+  auto plan = [&](int s, int b) {
+    CopyPlan c;
+    const int p = s / groups, hg = s - p * groups;
+    c.tok = t0 + __builtin_amdgcn_readfirstlane(s_tok[p]);
+    c.h0 = kKwHeads * hg;
+    c.hmax = min(kKwHeads - 1, num_heads - 1 - c.h0);
+    c.bb = lds_offset(&s_buf[b][0]);
+    c.qt = q_ptr + c.tok * q_st;
+    c.qb = (uint64_t)(c.qt + (int64_t)c.h0 * q_sh);
+    c.db = (uint64_t)(do_ptr + c.tok * do_st + (int64_t)c.h0 * do_sh);
+    return c;
+  };
+  auto copy = [&](const CopyPlan& c, int k) {
+    if (k < 16) {
+      const int h = wave + 4 * (k & 7), hr = min(h, c.hmax);
+      if (k < 8) dma_16b_sbase(c.qb + (uint64_t)(hr * q_sh2), cp_off[k & 3], c.bb + kKwQL + h * 1024);
+      else dma_16b_sbase(c.db + (uint64_t)(hr * do_sh2), cp_off[k & 3], c.bb + kKwDO + h * 1024);
+    } else if (k == 16) {
       const int h = 8 * wave + (lane >> 3);
-      const int hq = min(h0 + h, num_heads - 1);
-      dma_16b(qt + hq * q_sh + kDv + 8 * ((lane & 7) ^ kw_swz_r(h)), bb + kKwQR + 8 * wave * 128);
-    }
-    if (wave == 0) {
-      const int hq = min(h0 + (lane & 31), num_heads - 1);
-      dma_4b(lane < 32 ? lse_ptr + tok * lse_st + hq : d_ptr + tok * d_st + hq, bb + kKwLD);
+      const int hq = c.h0 + min(h, c.hmax);
+      dma_16b(c.qt + hq * q_sh + kDv + 8 * ((lane & 7) ^ kw_swz_r(h)), c.bb + kKwQR + 8 * wave * 128);
+    } else if (wave == 0) {
+      const int hq = c.h0 + min(lane & 31, c.hmax);
+      dma_4b(lane < 32 ? lse_ptr + c.tok * lse_st + hq : d_ptr + c.tok * d_st + hq, c.bb + kKwLD);
     }
   };
 
-  // dkv of the wave's rows: lane (g, n) holds column 16k + n of rows 16w + 4g + e
-  float4_t acc[kDqk / 16];
+  // dkv of the wave's rows and columns: acc[rt][k], lane (g, n) holds column
+  // tile k's column n of rows 32rh + 16rt + 4g + e (tiles k < 16: latent
+  // columns 256ch + 16k ..; k = 16, 17: rope columns 32ch + 16(k - 16) ..)
+  float4_t acc[2][18];
 #pragma unroll
-  for (int k = 0; k < kDqk / 16; ++k) acc[k] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int k = 0; k < 18; ++k) acc[rt][k] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  // Per-lane LDS offsets (within a step buffer). A-operand reads of row
-  // 16ht + n, latent granule 4c + g: 256 (c >> 2) + a_lat[c & 3] (the XOR
-  // only touches the granule's low 4 bits); rope granule 4c' + g: a_rope[c'].
-  // Transposed reads of rows hr = 4g + n/4 and 16 + hr, columns 16k + 4(n&3):
-  // 256 (k >> 3) + t_lat[k & 7]; rope column tile k': t_rope[k'].
-  uint32_t a_lat[4], a_rope[2], t_lat[8], t_rope[4];
+  // Per-lane LDS offsets within a step buffer. A-operand reads of row
+  // 16ht + n: latent chunk 8ch + j at 256 ((8ch + j) >> 2) + a_lat[j & 3]
+  // (the XOR only touches a granule index's low 4 bits), the rope half at
+  // a_rope. Transposed reads of rows hr = 4g + n/4 and 16 + hr, latent column
+  // tile 16ch + k: 256 ((16ch + k) >> 3) + t_lat[k & 7]; rope tiles: t_rope[i].
+  uint32_t a_lat[4], a_rope, t_lat[8], t_rope[2];
   {
     const int hr = 4 * g + (n >> 2), hb = (n >> 1) & 1;
 #pragma unroll
     for (int c = 0; c < 4; ++c) a_lat[c] = (uint32_t)(n * 1024 + 16 * ((4 * c + g) ^ kw_swz(n)));
-#pragma unroll
-    for (int c = 0; c < 2; ++c) a_rope[c] = (uint32_t)(kKwQR + n * 128 + 16 * ((4 * c + g) ^ kw_swz_r(n)));
+    a_rope = (uint32_t)(kKwQR + n * 128 + 16 * ((4 * ch + g) ^ kw_swz_r(n)));
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       t_lat[k] = (uint32_t)(hr * 1024 + 16 * ((2 * k + hb) ^ kw_swz(hr)) + 8 * (n & 1));
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      t_rope[k] = (uint32_t)(kKwQR + hr * 128 + 16 * ((2 * k + hb) ^ kw_swz_r(hr)) + 8 * (n & 1));
+    for (int i = 0; i < 2; ++i)
+      t_rope[i] = (uint32_t)(kKwQR + hr * 128 + 16 * ((2 * (2 * ch + i) + hb) ^ kw_swz_r(hr)) + 8 * (n & 1));
   }
+  // exchange area of the pair: region X[w] is wave w's 4 KB
+  const kw_lds* const xr_own = (const kw_lds*)&s_x[wave][0];
+  const kw_lds* const xr_pair = (const kw_lds*)&s_x[wave ^ 1][0];
   // The compiler does not see the asm copies' waits: make the K loads
   // complete here, with a wait it sees, so that it puts none in the loop
   // (there it would wait for the copies of the next step as well).
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-  issue(0, 0);
+  {
+    const CopyPlan c0 = plan(0, 0);
+#pragma unroll
+    for (int k = 0; k < 18; ++k) copy(c0, k);
+  }
   for (int s = 0; s < nsteps; ++s) {
     wait_vmem<0>();
     __syncthreads();
-    if (s + 1 < nsteps) issue(s + 1, (s + 1) & 1);
+    // the next step's copies go into the other buffer (free: its last reads
+    // were in the previous step, before this barrier); the last step copies
+    // its own token again (valid data nobody reads), so the copy stream has
+    // no branch, and the kernel drains it before it ends
+    const CopyPlan cn = plan(s + 1 < nsteps ? s + 1 : s, (s + 1) & 1);
     // LDS pointers of this step's buffer: the constant parts of each read's
     // address then fold into the instruction's offset field
     const kw_lds* const buf = (const kw_lds*)&s_buf[s & 1][0];
     const kw_lds* pa[4];
-    const kw_lds* pr[2];
     const kw_lds* pt[8];
-    const kw_lds* ptr_[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) pa[c] = buf + a_lat[c];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) pr[c] = buf + a_rope[c];
-#pragma unroll
     for (int k = 0; k < 8; ++k) pt[k] = buf + t_lat[k];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) ptr_[k] = buf + t_rope[k];
+    const kw_lds* const prope = buf + a_rope;
     const int p = s / groups, hg = s - p * groups;
     const int h0 = kKwHeads * hg;
     const uint64_t msk = s_msk[p];
     const float4_t l4[2] = {kw_f4(buf + kKwLD + 16 * g), kw_f4(buf + kKwLD + 64 + 16 * g)};
     const float4_t d4[2] = {kw_f4(buf + kKwLD + 128 + 16 * g), kw_f4(buf + kKwLD + 192 + 16 * g)};
 
-    // ---- S^T (16 heads x 16 rows, per head tile) over 576 columns, dP^T
-    // over 512: 68 A-operand reads, each feeding one MFMA, kRingA reads
-    // ahead (the order is pinned: the scheduler would otherwise sink each
-    // read next to its product). Read i < 64: chunk c = i / 4, head tile
-    // i & 1, q (i & 2 == 0) or dO; i >= 64: rope chunk (i - 64) / 2.
-    constexpr int kReadsA = 68, kRingA = 12;
+    // ---- partial S^T and dP^T over the wave's columns: [head tile ht][row tile rt].
+    // 34 A-operand reads (q: chunks j = 0..8, dO: j = 0..7, both head
+    // tiles), each feeding two MFMAs, kRingA reads ahead; the order is
+    // pinned (the scheduler would sink each read next to its products).
+    // Read i: j = i / 4, head tile i & 1, q (i & 2 == 0) or dO; i = 32, 33:
+    // the rope chunk of head tile i & 1.
+    constexpr int kReadsA = 34, kRingA = 14;
     auto a_read = [&](int i) -> bf16x8_t {
-      if (i < 64) {
-        const int c = i >> 2, ht = i & 1, isdo = (i >> 1) & 1;
-        return kw_b128(pa[c & 3] + (isdo ? kKwDO : kKwQL) + 16 * 1024 * ht + 256 * (c >> 2));
+      if (i < 32) {
+        const int j = i >> 2, ht = i & 1, isdo = (i >> 1) & 1;
+        return kw_b128(pa[j & 3] + (isdo ? kKwDO : kKwQL) + 16 * 1024 * ht + 256 * ((8 * ch + j) >> 2));
       }
-      return kw_b128(pr[(i - 64) >> 1] + 16 * 128 * (i & 1));
+      return kw_b128(prope + 16 * 128 * (i & 1));
     };
-    float4_t sacc[2], dacc[2];
+    float4_t sacc[2][2], dacc[2][2];
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) sacc[ht] = dacc[ht] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) sacc[ht][rt] = dacc[ht][rt] = (float4_t){0.f, 0.f, 0.f, 0.f};
     bf16x8_t ra[kRingA];
 #pragma unroll
     for (int i = 0; i < kRingA; ++i) ra[i] = a_read(i);
@@ -256,25 +296,47 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
     for (int i = 0; i < kReadsA; ++i) {
       const bf16x8_t v = ra[i % kRingA];
       if (i + kRingA < kReadsA) ra[i % kRingA] = a_read(i + kRingA);
-      const int c = i < 64 ? i >> 2 : kDv / 32 + ((i - 64) >> 1);
+      if ((i & 1) == 0) copy(cn, i >> 1);
+      if (i == 1) copy(cn, 17);
+      const int j = i < 32 ? i >> 2 : 8;
       const int ht = i & 1;
-      if (i < 64 && ((i >> 1) & 1))
-        dacc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, kreg[c], dacc[ht], 0, 0, 0);
-      else
-        sacc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, kreg[c], sacc[ht], 0, 0, 0);
+      const bool isdo = i < 32 && ((i >> 1) & 1);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        if (isdo)
+          dacc[ht][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, kreg[rt][j], dacc[ht][rt], 0, 0, 0);
+        else
+          sacc[ht][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, kreg[rt][j], sacc[ht][rt], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    // ---- the pair sums its partials: the wave keeps head tile ch and sends
+    // tile 1 - ch (S and dP of both row tiles: four float4 per lane)
+    {
+      float4_t* xo = (float4_t*)&s_x[wave][0];
+      xo[0 * 64 + lane] = sacc[1 - ch][0];
+      xo[1 * 64 + lane] = sacc[1 - ch][1];
+      xo[2 * 64 + lane] = dacc[1 - ch][0];
+      xo[3 * 64 + lane] = dacc[1 - ch][1];
+    }
+    __syncthreads();
+    float4_t sc[2], dc[2];
+    sc[0] = sacc[ch][0] + kw_f4(xr_pair + 16 * (0 * 64 + lane));
+    sc[1] = sacc[ch][1] + kw_f4(xr_pair + 16 * (1 * 64 + lane));
+    dc[0] = dacc[ch][0] + kw_f4(xr_pair + 16 * (2 * 64 + lane));
+    dc[1] = dacc[ch][1] + kw_f4(xr_pair + 16 * (3 * 64 + lane));
+
     // ---- transposed operands of the dkv product, kRingT column tiles ahead
-    // (q^T and dO^T of tile k: 4 reads; rope tiles: 2)
+    // (tile k < 16: q^T and dO^T, 4 reads; rope tiles k = 16, 17: q^T, 2)
     constexpr int kRingT = 4;
     auto t_read = [&](int k, bf16x8_t& bq, bf16x8_t& bo) {
-      if (k < kDv / 16) {
-        const kw_lds* o = pt[k & 7] + 256 * (k >> 3);
+      if (k < 16) {
+        const kw_lds* o = pt[k & 7] + 256 * ((16 * ch + k) >> 3);
         bq = join4(kw_tr(o + kKwQL), kw_tr(o + kKwQL + 16 * 1024));
         bo = join4(kw_tr(o + kKwDO), kw_tr(o + kKwDO + 16 * 1024));
       } else {
-        const kw_lds* o = ptr_[k - kDv / 16];
+        const kw_lds* o = buf + t_rope[k - 16];
         bq = join4(kw_tr(o), kw_tr(o + 16 * 128));
         bo = bq;
       }
@@ -283,47 +345,76 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
 #pragma unroll
     for (int k = 0; k < kRingT; ++k) t_read(k, rq[k], ro[k]);
 
-    // ---- P and s*dS: lane (g, n) has row 16w + n, heads h0 + 16ht + 4g + e
-    const bool rowok = (msk >> (16 * wave + n)) & 1u;
-    float pv[2][4], dsv[2][4];
+    // ---- P and s*dS of head tile ch: lane (g, n) has rows 32rh + 16rt + n,
+    // heads h0 + 16ch + 4g + e; packed bf16 (4 per row tile, P then dS)
+    uint32_t own[2][4];   // [rt][P lo, P hi, dS lo, dS hi]
+    {
+      const float4_t lc = ch ? l4[1] : l4[0], dd = ch ? d4[1] : d4[0];
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
+      for (int rt = 0; rt < 2; ++rt) {
+        const bool rowok = (msk >> (32 * rh + 16 * rt + n)) & 1u;
+        float pv[4], dsv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ok = rowok && h0 + 16 * ht + 4 * g + e < num_heads;
-        pv[ht][e] = ok ? __builtin_amdgcn_exp2f(sacc[ht][e] * scale_log2 - l4[ht][e] * 1.4426950408889634f) : 0.f;
-        dsv[ht][e] = pv[ht][e] * (dacc[ht][e] - d4[ht][e]) * scale;
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = rowok && h0 + 16 * ch + 4 * g + e < num_heads;
+          pv[e] = ok ? __builtin_amdgcn_exp2f(sc[rt][e] * scale_log2 - lc[e] * 1.4426950408889634f) : 0.f;
+          dsv[e] = pv[e] * (dc[rt][e] - dd[e]) * scale;
+        }
+        own[rt][0] = pack_bf16x2(pv[0], pv[1]);
+        own[rt][1] = pack_bf16x2(pv[2], pv[3]);
+        own[rt][2] = pack_bf16x2(dsv[0], dsv[1]);
+        own[rt][3] = pack_bf16x2(dsv[2], dsv[3]);
       }
-    const bf16x8_t a_ds = __builtin_bit_cast(
-        bf16x8_t, (u32x4_t){pack_bf16x2(dsv[0][0], dsv[0][1]), pack_bf16x2(dsv[0][2], dsv[0][3]),
-                            pack_bf16x2(dsv[1][0], dsv[1][1]), pack_bf16x2(dsv[1][2], dsv[1][3])});
-    const bf16x8_t a_p = __builtin_bit_cast(
-        bf16x8_t, (u32x4_t){pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
-                            pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])});
+    }
+    // ... and exchanges them: written to the region just read (the pair's),
+    // read from the wave's own (the pair writes there)
+    {
+      u32x4_t* xo = (u32x4_t*)&s_x[wave ^ 1][0];
+      xo[0 * 64 + lane] = (u32x4_t){own[0][0], own[0][1], own[0][2], own[0][3]};
+      xo[1 * 64 + lane] = (u32x4_t){own[1][0], own[1][1], own[1][2], own[1][3]};
+    }
+
+    __syncthreads();
+    bf16x8_t a_p[2], a_ds[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const u32x4_t o = *(__attribute__((address_space(3))) const u32x4_t*)(xr_own + 16 * (rt * 64 + lane));
+      // k-slots 8g .. 8g+3: heads 4g .. (head tile 0), 8g+4 .. 8g+7: 16 + 4g .. (tile 1)
+      const u32x4_t lo = ch ? o : (u32x4_t){own[rt][0], own[rt][1], own[rt][2], own[rt][3]};
+      const u32x4_t hi = ch ? (u32x4_t){own[rt][0], own[rt][1], own[rt][2], own[rt][3]} : o;
+      a_p[rt] = __builtin_bit_cast(bf16x8_t, (u32x4_t){lo[0], lo[1], hi[0], hi[1]});
+      a_ds[rt] = __builtin_bit_cast(bf16x8_t, (u32x4_t){lo[2], lo[3], hi[2], hi[3]});
+    }
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- dkv[16 rows x 16 columns] += (s dS) q + P dO over the 32 heads, per
-    // column tile; the two products of a tile are a tile apart
-    bf16x8_t bo_prev = {};
+    // ---- dkv[2 row tiles x 16 columns] += (s dS) q + P dO over the 32 heads, per column tile
 #pragma unroll
-    for (int k = 0; k < kDqk / 16; ++k) {
+    for (int k = 0; k < 18; ++k) {
       const bf16x8_t bq = rq[k % kRingT], bo = ro[k % kRingT];
-      if (k + kRingT < kDqk / 16) t_read(k + kRingT, rq[k % kRingT], ro[k % kRingT]);
-      acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_ds, bq, acc[k], 0, 0, 0);
-      if (k >= 1 && k - 1 < kDv / 16)
-        acc[k - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p, bo_prev, acc[k - 1], 0, 0, 0);
-      bo_prev = bo;
+      if (k + kRingT < 18) t_read(k + kRingT, rq[k % kRingT], ro[k % kRingT]);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) acc[rt][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_ds[rt], bq, acc[rt][k], 0, 0, 0);
+      if (k < 16) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) acc[rt][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p[rt], bo, acc[rt][k], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
+  wait_vmem<0>();   // the last step's copies land before the workgroup's LDS is released
+
   // ---- the rows' dkv, once per workgroup (other chunks add to the same rows)
 #pragma unroll
-  for (int k = 0; k < kDqk / 16; ++k)
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t r = r0 + 16 * wave + 4 * g + e;
-      if (r < a.num_kv) unsafeAtomicAdd(a.dkv + r * a.dkv_st + 16 * k + n, acc[k][e]);
+    for (int k = 0; k < 18; ++k) {
+      const int col = k < 16 ? 256 * ch + 16 * k + n : kDv + 32 * ch + 16 * (k - 16) + n;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t r = r0 + 32 * rh + 16 * rt + 4 * g + e;
+        if (r < a.num_kv) unsafeAtomicAdd(a.dkv + r * a.dkv_st + col, acc[rt][k][e]);
+      }
     }
 }
 

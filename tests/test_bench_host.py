@@ -117,8 +117,15 @@ def test_trace_summary(tmp_path):
 
 def test_counter_summary(tmp_path):
     """Counters per dispatch of the op's kernel only; MFMA-busy fraction
-    against GRBM_GUI_ACTIVE x 1024 SIMDs, L2 hit fraction from TCC hits and misses."""
+    against the SIMD count (from the agent info) x the dispatch's cycles
+    (SQ_BUSY_CYCLES over the shader engines), L2 hit fraction from TCC hits
+    and misses."""
     import argparse
+    with open(tmp_path / "pmc_agent_info.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Agent_Type", "Name", "Simd_Count", "Num_Shader_Banks"])
+        w.writeheader()
+        w.writerow({"Agent_Type": "CPU", "Name": "host", "Simd_Count": 0, "Num_Shader_Banks": 0})
+        w.writerow({"Agent_Type": "GPU", "Name": "gfx950", "Simd_Count": 1024, "Num_Shader_Banks": 32})
     p = tmp_path / "pmc.csv"
     with open(p, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
@@ -127,13 +134,13 @@ def test_counter_summary(tmp_path):
             k = "void dsa::sparse_mla_fwd_ws_kernel<false>(dsa::FwdArgs)"
             w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES",
                         "Counter_Value": 512000})
-            w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "GRBM_GUI_ACTIVE",
-                        "Counter_Value": 1000})
+            w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "SQ_BUSY_CYCLES",
+                        "Counter_Value": 32000})
             w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "TCC_HIT_sum", "Counter_Value": 75})
             w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "TCC_MISS_sum", "Counter_Value": 25})
-        w.writerow({"Dispatch_Id": 9, "Kernel_Name": "at::neg", "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": 5})
+        w.writerow({"Dispatch_Id": 9, "Kernel_Name": "at::neg", "Counter_Name": "SQ_BUSY_CYCLES", "Counter_Value": 5})
     args = argparse.Namespace(op="fwd", workload="wide", traffic_command="cmd")
     bench.summarize_counters(args, [str(p)], out_dir=str(tmp_path))
     out = json.load(open(tmp_path / "counters_fwd_wide.json"))
     assert out["mfma_busy_frac"] == 0.5 and out["l2_hit_frac"] == 0.75
-    assert out["dispatches"]["GRBM_GUI_ACTIVE"] == 3
+    assert out["dispatches"]["SQ_BUSY_CYCLES"] == 3 and out["cycles_per_dispatch"] == 1000
