@@ -391,17 +391,32 @@ def test_full_size_sampled(name, nsample):
     check(np32(out)[toks], np32(lse)[toks], ro, rl, f"{name} full, {len(toks)} sampled tokens")
 
 
-def test_decode_full_size_sampled():
+def test_decode_full_size_all_sequences():
+    """The decode workload at full size (64 sequences x 6 tokens, contexts up
+    to 65536, paged bf16 cache), in the launch configuration bench.py times;
+    every token against the oracle. The oracle takes eight sequences at a
+    time with only their pages (compacted and renumbered), which bounds its
+    memory."""
     d = workloads.make_paged(device="cuda")
     dsa = _dsa()
     out, lse = dsa.sparse_mla_fwd_paged(d["q"], d["kv_pages"], d["page_table"], d["seq_lens"],
                                         d["indices"], d["sm_scale"], d["q_per_seq"])
     torch.cuda.synchronize()
-    seqs = np.array([0, 17, 40, 63])
-    toks = (seqs[:, None] * 6 + np.arange(6)).ravel()
-    tt = torch.from_numpy(toks).to(DEV)
-    ro, rl = sparse_mla_fwd_paged_ref(
-        np32(d["q"][tt]), np32(d["kv_pages"]), d["page_table"][torch.from_numpy(seqs).to(DEV)].cpu().numpy(),
-        d["seq_lens"][torch.from_numpy(seqs).to(DEV)].cpu().numpy(), d["indices"][tt].cpu().numpy(),
-        d["sm_scale"], 6)
-    check(np32(out)[toks], np32(lse)[toks], ro, rl, "decode full, 4 sampled sequences")
+    Q = d["q_per_seq"]
+    S = d["page_table"].shape[0]
+    table_all = d["page_table"].cpu().numpy()
+    lens_all = d["seq_lens"].cpu().numpy()
+    o_all, l_all = np32(out), np32(lse)
+    for s0 in range(0, S, 8):
+        seqs = np.arange(s0, min(S, s0 + 8))
+        toks = (seqs[:, None] * Q + np.arange(Q)).ravel()
+        table = table_all[seqs]
+        used = np.unique(table[table >= 0])
+        remap = np.full(d["kv_pages"].shape[0], -1, dtype=np.int64)
+        remap[used] = np.arange(used.size)
+        small = np.where(table >= 0, remap[np.maximum(table, 0)], -1).astype(np.int32)
+        pages = np32(d["kv_pages"][torch.from_numpy(used).to(DEV)])
+        tt = torch.from_numpy(toks).to(DEV)
+        ro, rl = sparse_mla_fwd_paged_ref(np32(d["q"][tt]), pages, small, lens_all[seqs],
+                                          d["indices"][tt].cpu().numpy(), d["sm_scale"], Q)
+        check(o_all[toks], l_all[toks], ro, rl, f"decode full, sequences {s0}..{seqs[-1]}")
