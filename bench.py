@@ -50,10 +50,21 @@ BWD_FLOP_PER_KEY_HEAD = 2 * (3 * 576 + 2 * 512)
 BWD_BYTES_PER_KEY = ROW_BYTES
 
 
-def source_hash() -> str:
+# kernel sources behind each op's measurements (the launch code is in the .hip)
+OP_SOURCES = {
+    "fwd": ("dsa_sparse_mla.hip", "fwd_kernel.hpp", "fwd_kernel_ws.hpp"),
+    "bwd": ("dsa_sparse_mla.hip", "fwd_kernel.hpp", "bwd_kernel.hpp", "bwd_kvw_kernel.hpp"),
+    "topk": ("dsa_sparse_mla.hip", "topk_kernel.hpp"),
+}
+
+
+def source_hash(op: str | None = None) -> str:
+    """Hash of the kernel sources an op's profiles were taken on (all of
+    csrc/ when op is None): a profile stays valid while they are unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dsa_sparse_mla_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    names = sorted(os.listdir(csrc)) if op is None else sorted(OP_SOURCES[op])
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -73,7 +84,7 @@ def traffic_for(workload: str, op: str = "fwd"):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash(op):
         return None
     return rec.get("bytes_per_launch")
 
@@ -121,7 +132,7 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: st
                 vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
         return vals
 
-    out = {"workload": workload, "source_hash": source_hash(), "command": command}
+    out = {"workload": workload, "op": op, "source_hash": source_hash(op), "command": command}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         vals = per_dispatch(path, counter)
         copy = [v for (d, k), v in vals.items() if "neg" in k]
@@ -219,9 +230,11 @@ def summarize_trace(args, trace_dir: str, log_path: str, out_dir: str | None = N
 
 
 def summarize_counters(args, csv_paths, out_dir: str | None = None):
-    """Median per dispatch of every counter in rocprofv3 --pmc CSVs, for the
-    op's kernel, into profiles/counters_<op>_<workload>.json, with derived
-    MFMA-busy, L2 hit and LDS bank-conflict fractions.
+    """Median per dispatch of every counter in rocprofv3 --pmc CSVs, per
+    kernel of the op, into profiles/counters_<op>_<workload>.json, with
+    derived MFMA-busy, L2 hit and LDS bank-conflict fractions. The top-level
+    figures are those of the kernel with the most busy cycles (an op such as
+    the backward launches several kernels per call).
 
     SQ counters are summed over the shader engines, so a dispatch's cycles
     are SQ_BUSY_CYCLES / Num_Shader_Banks (32 on MI355X), and the MFMA-busy
@@ -231,21 +244,19 @@ def summarize_counters(args, csv_paths, out_dir: str | None = None):
     import csv
     import statistics
     kern = OP_KERNEL[args.op]
-    per = {}
-    names = set()
+    per = {}   # kernel -> counter -> dispatch -> value
     for path in csv_paths:
         with open(path) as f:
             for row in csv.DictReader(f):
-                if not kern.search(row.get("Kernel_Name", "")):
+                name = row.get("Kernel_Name", "")
+                if not kern.search(name):
                     continue
                 key = (path, row["Dispatch_Id"])
                 c = row["Counter_Name"]
-                names.add(row["Kernel_Name"])
-                per.setdefault(c, {}).setdefault(key, 0.0)
-                per[c][key] += float(row["Counter_Value"])
+                d = per.setdefault(name, {}).setdefault(c, {})
+                d[key] = d.get(key, 0.0) + float(row["Counter_Value"])
     if not per:
         raise SystemExit("no dispatch of the op's kernel in the counter files")
-    med = {c: statistics.median(v.values()) for c, v in per.items()}
     simds, engines = 1024, 32
     for path in csv_paths:
         info = os.path.join(os.path.dirname(path), "pmc_agent_info.csv")
@@ -257,18 +268,28 @@ def summarize_counters(args, csv_paths, out_dir: str | None = None):
                         engines = int(row.get("Num_Shader_Banks") or engines)
                         break
             break
-    out = {"workload": args.workload, "op": args.op, "source_hash": source_hash(),
-           "kernels": sorted(names), "dispatches": {c: len(v) for c, v in per.items()}, "counters": med,
-           "simds": simds, "shader_engines": engines, "command": args.traffic_command}
-    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and med.get("SQ_BUSY_CYCLES"):
-        cycles = med["SQ_BUSY_CYCLES"] / engines
-        out["cycles_per_dispatch"] = cycles
-        out["mfma_busy_frac"] = round(med["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cycles), 4)
-    hit, miss = med.get("TCC_HIT_sum"), med.get("TCC_MISS_sum")
-    if hit is not None and miss is not None and hit + miss > 0:
-        out["l2_hit_frac"] = round(hit / (hit + miss), 4)
-    if med.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in med:
-        out["lds_conflict_frac"] = round(med["SQ_LDS_BANK_CONFLICT"] / med["SQ_LDS_IDX_ACTIVE"], 4)
+
+    def derive(counters):
+        med = {c: statistics.median(v.values()) for c, v in counters.items()}
+        out = {"dispatches": {c: len(v) for c, v in counters.items()}, "counters": med}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med and med.get("SQ_BUSY_CYCLES"):
+            cycles = med["SQ_BUSY_CYCLES"] / engines
+            out["cycles_per_dispatch"] = cycles
+            out["mfma_busy_frac"] = round(med["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cycles), 4)
+        hit, miss = med.get("TCC_HIT_sum"), med.get("TCC_MISS_sum")
+        if hit is not None and miss is not None and hit + miss > 0:
+            out["l2_hit_frac"] = round(hit / (hit + miss), 4)
+        if med.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in med:
+            out["lds_conflict_frac"] = round(med["SQ_LDS_BANK_CONFLICT"] / med["SQ_LDS_IDX_ACTIVE"], 4)
+        return out
+
+    kernels = {name: derive(c) for name, c in per.items()}
+    main = max(kernels, key=lambda n: kernels[n]["counters"].get("SQ_BUSY_CYCLES", 0.0))
+    out = {"workload": args.workload, "op": args.op, "source_hash": source_hash(args.op),
+           "kernel": main, **kernels[main], "simds": simds, "shader_engines": engines,
+           "command": args.traffic_command}
+    if len(kernels) > 1:
+        out["per_kernel"] = kernels
     path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"counters_{args.op}_{args.workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -692,7 +713,7 @@ def main():
                "kernel_ms_avg": round(avg, 5), "kernel_ms_median": round(med, 5),
                "roofline": {"bound": "hbm", "achieved": round(kern, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(kern / HBM_PEAK_GBPS, 4), "traffic": traffic_for(args.workload, "topk")},
-               "source_hash": source_hash()}
+               "source_hash": source_hash("topk")}
         if args.cpu_budget > 0:
             rec["cpu_baseline"] = cpu_baseline_topk(tk, args.cpu_budget)
         print(json.dumps(rec), flush=True)
@@ -775,7 +796,7 @@ def main():
         **({"kernel_ms_flushed": round(flushed_ms, 5),
             "gathered_kv_gbps_flushed": round(gathered / (flushed_ms * 1e-3) / 1e9, 2)}
            if flushed_ms is not None else {}),
-        "source_hash": source_hash(),
+        "source_hash": source_hash(args.op),
     }
     if args.op == "bwd":
         rec["config"]["op"] = "bwd"

@@ -42,7 +42,24 @@ def test_traffic_summary_scales_by_the_copy(tmp_path):
     assert rec["fetch_factor"] == 2.0 and rec["write_factor"] == 1.0
     assert rec["fetch_bytes"] == 2 * 1000 * 1024 and rec["write_bytes"] == 300 * 1024
     assert rec["bytes_per_launch"] == rec["fetch_bytes"] + rec["write_bytes"]
-    assert rec["fetch_dispatches"] == 2 and rec["source_hash"] == bench.source_hash()
+    assert rec["fetch_dispatches"] == 2 and rec["source_hash"] == bench.source_hash("fwd")
+
+
+def test_source_hash_per_op(tmp_path, monkeypatch):
+    """An op's profiles depend only on its kernels and the launch code: a
+    change to the backward's kernel leaves the forward's hash alone."""
+    csrc = tmp_path / "dsa_sparse_mla_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for name in ("dsa_sparse_mla.hip", "fwd_kernel.hpp", "fwd_kernel_ws.hpp", "bwd_kernel.hpp",
+                 "bwd_kvw_kernel.hpp", "topk_kernel.hpp"):
+        (csrc / name).write_text(name)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    before = {op: bench.source_hash(op) for op in ("fwd", "bwd", "topk")}
+    full = bench.source_hash()
+    (csrc / "bwd_kvw_kernel.hpp").write_text("changed")
+    after = {op: bench.source_hash(op) for op in ("fwd", "bwd", "topk")}
+    assert after["fwd"] == before["fwd"] and after["topk"] == before["topk"]
+    assert after["bwd"] != before["bwd"] and bench.source_hash() != full
 
 
 def test_backward_traffic_sums_the_kernels_of_a_call(tmp_path):
@@ -144,3 +161,25 @@ def test_counter_summary(tmp_path):
     out = json.load(open(tmp_path / "counters_fwd_wide.json"))
     assert out["mfma_busy_frac"] == 0.5 and out["l2_hit_frac"] == 0.75
     assert out["dispatches"]["SQ_BUSY_CYCLES"] == 3 and out["cycles_per_dispatch"] == 1000
+
+
+def test_counter_summary_per_kernel(tmp_path):
+    """An op with several kernels per call (the backward): each kernel gets
+    its own medians, and the top-level figures are the busiest kernel's."""
+    import argparse
+    p = tmp_path / "pmc.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for disp, k, busy, mfma in ((1, "dsa::dkv_zero_kernel(float*, long, long)", 3200, 0),
+                                    (2, "dsa::sparse_mla_bwd_kvw_kernel(dsa::BwdArgs, dsa::KvMajorArgs)", 320000, 2048000),
+                                    (3, "void dsa::sparse_mla_bwd_kernel<2, false>(dsa::BwdArgs)", 160000, 512000)):
+            w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "SQ_BUSY_CYCLES", "Counter_Value": busy})
+            w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES",
+                        "Counter_Value": mfma})
+    args = argparse.Namespace(op="bwd", workload="wide", traffic_command="cmd")
+    bench.summarize_counters(args, [str(p)], out_dir=str(tmp_path))
+    out = json.load(open(tmp_path / "counters_bwd_wide.json"))
+    assert "kvw" in out["kernel"] and out["mfma_busy_frac"] == 0.2   # 2048000 / (1024 * 320000 / 32)
+    assert len(out["per_kernel"]) == 3
+    assert out["per_kernel"]["void dsa::sparse_mla_bwd_kernel<2, false>(dsa::BwdArgs)"]["mfma_busy_frac"] == 0.1
