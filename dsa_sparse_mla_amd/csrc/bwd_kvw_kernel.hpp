@@ -34,9 +34,9 @@
 // LDS per step buffer: q latent [32 heads][1024 B], q rope [32][128 B],
 // dO [32][1024 B], then LSE and D [2][32] fp32: 69888 B, two buffers.
 // Granule G (16 B) of latent/dO row h sits at G ^ kw_swz(h) (within its
-// 256-byte group), rope granule G at G ^ kw_swz_r(h): the A-operand reads
-// (16 rows at one granule) and the transposed reads (8 rows x 32 B) are then
-// free of bank conflicts.
+// 256-byte group), rope granule G at G ^ kw_swz_r(h), so that the A-operand
+// reads (16 rows at one granule) and the transposed reads (8 rows x 32 B
+// per half-wave) are free of bank conflicts.
 //
 // Pages: the prime-rl pull request 4078 that adds a `cudnn_flashmla` DSA
 // backend (a separate DSA backward kernel, timed per call); "[Feature] Add
@@ -71,8 +71,13 @@ __device__ __forceinline__ short4_t kw_tr(const kw_lds* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)p);
 }
 
-__host__ __device__ constexpr int kw_swz(int h) { return 2 * ((h & 7) ^ ((h >> 1) & 4)); }
-__host__ __device__ constexpr int kw_swz_r(int h) { return 2 * (((h >> 1) & 3) ^ ((h >> 2) & 2)); }
+// Chosen by measurement (SQ_LDS_BANK_CONFLICT on probes of both read
+// patterns): the transposed reads need (swizzle >> 1) distinct over rows
+// 0..7 and over 8..15; the A-operand reads (16 rows at one logical
+// granule) are conflict-free with these and, e.g., with the identity, but
+// not with every XOR that is a bijection on 16 rows.
+__host__ __device__ constexpr int kw_swz(int h) { return (h & 6) | ((h & 1) << 3); }
+__host__ __device__ constexpr int kw_swz_r(int h) { return h & 6; }
 
 // One wave-wide 4-byte-per-lane copy HBM -> LDS: lane L's dword lands at LDS
 // byte lds_base + 4 * L (lds_base wave-uniform, in M0).
