@@ -173,13 +173,18 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
 
     // rows of tile t: thread tid holds granules tid + 256k (row = gi / 72, granule gi % 72)
     bf16x8_t greg[kBwGran];
+    // all row ids first, then all loads: one LDS round trip per tile, not one per load
     auto load_tile = [&](int t) {
+      uint32_t rid[kBwGran];
+#pragma unroll
+      for (int k = 0; k < kBwGran; ++k) rid[k] = s_rows[t * kTileKeys + (tid + 256 * k) / (kDqk / 8)];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < kBwGran; ++k) {
-        const int gi = tid + 256 * k, row = gi / (kDqk / 8), c = gi % (kDqk / 8);
-        const uint32_t rid = s_rows[t * kTileKeys + row];
-        greg[k] = *(const bf16x8_t*)(a.kv + (int64_t)rid * a.kv_st + 8 * c);
+        const int c = (tid + 256 * k) % (kDqk / 8);
+        greg[k] = *(const bf16x8_t*)(a.kv + (int64_t)rid[k] * a.kv_st + 8 * c);
       }
+      __builtin_amdgcn_sched_barrier(0);
     };
     auto store_tile = [&](int t) {
       uint8_t* st = s_stage[t & 1];
@@ -254,13 +259,24 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
         bf16x8_t ads[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) ads[ht] = lds16(s_dst + (16 * ht + n) * 64 + 16 * g);   // keys 8g ..
+        // K^T operands read 4 tiles ahead (pinned order: the scheduler would
+        // otherwise sink each read next to its products)
+        constexpr int kRA = 4;
+        bf16x8_t kb_ring[kRA];
+        auto kt_read = [&](int k) {
+          const int d0 = 16 * (9 * wave + k);
+          return join4(lds_read_tr16(kt + 2 * d0), lds_read_tr16(kt + 4 * kBwPitch + 2 * d0));
+        };
+#pragma unroll
+        for (int k = 0; k < kRA; ++k) kb_ring[k] = kt_read(k);
 #pragma unroll
         for (int k = 0; k < 9; ++k) {
-          const int d0 = 16 * (9 * wave + k);
-          const bf16x8_t b = join4(lds_read_tr16(kt + 2 * d0), lds_read_tr16(kt + 4 * kBwPitch + 2 * d0));
+          const bf16x8_t b = kb_ring[k % kRA];
+          if (k + kRA < 9) kb_ring[k % kRA] = kt_read(k + kRA);
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht)
             dq_acc[ht][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads[ht], b, dq_acc[ht][k], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // ---- phase 3b: dkv of key block kb2 = w >> 1, column tiles 18(w & 1) .. +17:
