@@ -21,8 +21,9 @@
 //            in registers); waves 2,3: dP^T = V dO^T likewise (dO^T in
 //            registers), handed to waves 0,1 through LDS;
 //   phase 2: waves 0,1: P and s*dS in bf16 into LDS, [head][32 keys];
-//   phase 3: every wave: dq (9 of the 36 16-column tiles) += (s dS) K, with
-//            K^T read transposed from the tile (ds_read_b64_tr_b16); and
+//   phase 3: every wave: dq column tiles 4k + w (k = 0..8) += (s dS) K,
+//            with K^T read transposed from the tile (ds_read_b64_tr_b16;
+//            the k slots of lane group g are keys 4g.., 16+4g..); and
 //            dkv tiles [16 keys x 16 columns] = (s dS)^T Q + P^T dO on
 //            16x16x16 MFMA over the 16 heads, added to the caller's fp32
 //            dkv with atomics (other tokens name the same rows).
@@ -67,8 +68,21 @@ struct BwdArgs {
   int32_t only_nonzero;    // 1: run the tokens with only[t] != 0; 0: those with only[t] == 0
 };
 
-constexpr int kBwPitch = 1168;                  // LDS row pitch of K rows and Q rows: 1152 + 16
-constexpr int kBwStage = kTileKeys * kBwPitch;  // one tile of 32 rows
+constexpr int kBwPitch = 1168;                  // LDS row pitch of Q rows (and kv-major K rows): 1152 + 16
+constexpr int kBwLat = kTileKeys * kDv * 2;     // stage of one tile: the 32 latent parts (1024 B each),
+constexpr int kBwStage = kBwLat + kTileKeys * (kDqk - kDv) * 2;   // then the 32 rope parts (128 B each)
+
+// Swizzles of the stage and of the dkv pass's step buffers: granule G (16 B)
+// of the latent part of row r sits at G ^ bw_swz(r) within its 256-byte
+// group, rope granule G at G ^ bw_swz_r(r). Chosen by measurement
+// (SQ_LDS_BANK_CONFLICT on probes of both read patterns): the transposed
+// reads (rows 4g + n/4 and 16 + 4g + n/4, 32 B per row and half-wave) need
+// (swizzle >> 1) distinct over rows 0..7 and over 8..15; the A-operand
+// reads (16 rows at one logical granule) are conflict-free with these and,
+// e.g., with the identity, but not with every XOR that is a bijection on
+// 16 rows.
+__host__ __device__ constexpr int bw_swz(int r) { return (r & 6) | ((r & 1) << 3); }
+__host__ __device__ constexpr int bw_swz_r(int r) { return r & 6; }
 constexpr int kBwOPitch = 1040;                 // LDS row pitch of dO rows: 1024 + 16
 constexpr int kBwGran = kTileKeys * (kDqk / 8) / 256;   // 16-byte granules per thread per tile (9)
 static_assert(kTileKeys * (kDqk / 8) % 256 == 0, "a tile splits evenly over the threads");
@@ -81,8 +95,7 @@ __device__ __forceinline__ bf16x8_t join4(short4_t lo, short4_t hi) {
 // HT head tiles of 16 per workgroup (1 or 2). With 2, each key's dkv row is
 // added once per 32 heads instead of once per 16, and each tile is gathered
 // once for 32 heads.
-// DKV = false compiles the dkv phase out: the dq pass of the split schedule.
-template <int HT, bool DKV = true>
+template <int HT>
 __global__ void __launch_bounds__(256)
 sparse_mla_bwd_kernel(const BwdArgs a) {
   constexpr int HB = 16 * HT;   // heads of the workgroup
@@ -90,8 +103,10 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_q[HB * kBwPitch];
   __shared__ __attribute__((aligned(16))) uint8_t s_do[HB * kBwOPitch];
   __shared__ __attribute__((aligned(16))) float4_t s_dp[2][HT][64];   // dP^T of key block 0 / 1, head tile
-  __shared__ __attribute__((aligned(16))) uint8_t s_pt[HB * 64];      // P, bf16 [head][32 keys]
-  __shared__ __attribute__((aligned(16))) uint8_t s_dst[HB * 64];     // s*dS, bf16 [head][32 keys]
+  // P and s*dS, bf16 [head][32 keys], keys in the dq products' k-slot order:
+  // bytes 16q .. 16q+7 hold keys 4q .. 4q+3, bytes 16q+8 .. 16q+15 keys 16+4q .. 16+4q+3
+  __shared__ __attribute__((aligned(16))) uint8_t s_pt[HB * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_dst[HB * 64];
   __shared__ __attribute__((aligned(16))) uint32_t s_rows[kSegment];  // compacted row ids
   __shared__ int s_cnt[kChunks];
   __shared__ float s_D[HB], s_lse2[HB];
@@ -151,12 +166,35 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
                            : (c < kDv / 32 ? lds16(s_do + (16 * ht + n) * kBwOPitch + 2 * (32 * c + 8 * g))
                                            : (bf16x8_t){});
 
-  // dq tiles 9w .. 9w+8 of head tile ht: lane holds column 16dt + n of heads 16ht + 4g .. +3
+  // dq column tiles m = 4k + w (k = 0 .. 8) of head tile ht: lane holds
+  // column 16m + n of heads 16ht + 4g .. +3
   float4_t dq_acc[HT][9];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
     for (int k = 0; k < 9; ++k) dq_acc[ht][k] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  // stage offsets of the lane's reads. Phase 1 (A operand): key kb*16 + n,
+  // logical granule 4c + g; latent c = 4i + c' at a_lat[c'] + 256i, rope c = 16 + c' at a_rope[c'].
+  uint32_t a_lat[4], a_rope[2];
+  {
+    const int r = kb * 16 + n;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a_lat[c] = (uint32_t)(r * 1024 + 16 * ((4 * c + g) ^ bw_swz(r)));
+#pragma unroll
+    for (int c = 0; c < 2; ++c) a_rope[c] = (uint32_t)(kBwLat + r * 128 + 16 * ((4 * c + g) ^ bw_swz_r(r)));
+  }
+  // Phase 3a (K^T operand of column tile m = 4k + w): lane (g, n) points at
+  // key 4g + n/4 (and 16 + 4g + n/4), columns 16m + 4(n % 4) ..; latent tile
+  // k at t_lat[k % 2] + 256 (k / 2), the rope tile (k = 8) at t_rope.
+  uint32_t t_lat[2], t_rope;
+  {
+    const int r = 4 * g + (n >> 2), hb = (n >> 1) & 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      t_lat[i] = (uint32_t)(r * 1024 + 16 * ((2 * (wave + 4 * i) + hb) ^ bw_swz(r)) + 8 * (n & 1));
+    t_rope = (uint32_t)(kBwLat + r * 128 + 16 * ((2 * wave + hb) ^ bw_swz_r(r)) + 8 * (n & 1));
+  }
 
   FwdArgs fa = {};   // the forward's index stage, with row ids as the offsets
   fa.idx = a.idx;
@@ -191,7 +229,9 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
 #pragma unroll
       for (int k = 0; k < kBwGran; ++k) {
         const int gi = tid + 256 * k, row = gi / (kDqk / 8), c = gi % (kDqk / 8);
-        *(bf16x8_t*)(st + row * kBwPitch + 16 * c) = greg[k];
+        uint8_t* d = c < kDv / 8 ? st + row * 1024 + 16 * (c ^ bw_swz(row))
+                                 : st + kBwLat + row * 128 + 16 * ((c - kDv / 8) ^ bw_swz_r(row));
+        *(bf16x8_t*)d = greg[k];
       }
     };
     if (ntiles > 0) {
@@ -206,13 +246,14 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
 
       // ---- phase 1: S^T (waves 0, 1) or dP^T (waves 2, 3) of key block kb, every head tile
       float4_t acc[HT];
-      const uint8_t* arow = st + (kb * 16 + n) * kBwPitch + 16 * g;   // key kb*16 + n, columns 8g ..
+      // key kb*16 + n, columns 32c + 8g ..
+      auto arow = [&](int c) { return c < 16 ? st + a_lat[c & 3] + 256 * (c >> 2) : st + a_rope[c - 16]; };
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) acc[ht] = (float4_t){0.f, 0.f, 0.f, 0.f};
       if (s_role) {
 #pragma unroll
         for (int c = 0; c < kDqk / 32; ++c) {
-          const bf16x8_t av = lds16(arow + 64 * c);
+          const bf16x8_t av = lds16(arow(c));
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht)
             acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, breg[ht][c], acc[ht], 0, 0, 0);
@@ -220,7 +261,7 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
       } else {
 #pragma unroll
         for (int c = 0; c < kDv / 32; ++c) {
-          const bf16x8_t av = lds16(arow + 64 * c);
+          const bf16x8_t av = lds16(arow(c));
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht)
             acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, breg[ht][c], acc[ht], 0, 0, 0);
@@ -245,27 +286,30 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
             p[e] = ok ? __builtin_amdgcn_exp2f(acc[ht][e] * a.scale_log2 - l2) : 0.f;
             ds[e] = p[e] * (dp[e] - Dh) * a.scale;
           }
-          const int off = h * 64 + 2 * (kb * 16 + 4 * g);
+          const int off = h * 64 + 16 * g + 8 * kb;   // keys kb*16 + 4g .. +3 (k-slot order)
           *(uint2*)(s_pt + off) = (uint2){pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
           *(uint2*)(s_dst + off) = (uint2){pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
         }
       }
       __syncthreads();
 
-      // ---- phase 3a: dq tiles 9w .. 9w+8 += (s dS)[16 heads x 32 keys] K[32 keys x 16 columns]
+      // ---- phase 3a: dq tiles 4k + w += (s dS)[16 heads x 32 keys] K[32 keys x 16 columns],
+      //      k slots 8g .. 8g+7 = keys 4g .. 4g+3, 16+4g .. 16+4g+3
       {
-        // K^T operand: lane (g, n) points at key 8g + 4half + n/4, columns d0 + 4(n % 4)
-        const uint8_t* kt = st + (8 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
         bf16x8_t ads[HT];
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) ads[ht] = lds16(s_dst + (16 * ht + n) * 64 + 16 * g);   // keys 8g ..
+        for (int ht = 0; ht < HT; ++ht) ads[ht] = lds16(s_dst + (16 * ht + n) * 64 + 16 * g);
         // K^T operands read 4 tiles ahead (pinned order: the scheduler would
         // otherwise sink each read next to its products)
         constexpr int kRA = 4;
         bf16x8_t kb_ring[kRA];
         auto kt_read = [&](int k) {
-          const int d0 = 16 * (9 * wave + k);
-          return join4(lds_read_tr16(kt + 2 * d0), lds_read_tr16(kt + 4 * kBwPitch + 2 * d0));
+          if (k < 8) {
+            const uint8_t* p = st + t_lat[k & 1] + 256 * (k >> 1);
+            return join4(lds_read_tr16(p), lds_read_tr16(p + 16 * 1024));
+          }
+          const uint8_t* p = st + t_rope;
+          return join4(lds_read_tr16(p), lds_read_tr16(p + 16 * 128));
         };
 #pragma unroll
         for (int k = 0; k < kRA; ++k) kb_ring[k] = kt_read(k);
@@ -281,7 +325,7 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
       }
       // ---- phase 3b: dkv of key block kb2 = w >> 1, column tiles 18(w & 1) .. +17:
       //   [16 keys x 16 columns] = (s dS)^T Q + P^T dO over the HB heads
-      if constexpr (DKV) {
+      {
         const int kb2 = wave >> 1;
         const int kbase = j * kTileKeys + kb2 * 16 + 4 * g;   // this lane's outputs: keys kbase + e
         uint32_t rid[4];
@@ -294,7 +338,7 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
         if constexpr (HT == 1) {
           // 16x16x16 over heads 4g .. 4g+3: A operands (lane (g, n) points at head
           // 4g + n/4, keys kb2*16 + 4(n % 4)) receive key kb2*16 + n
-          const int aoff = (4 * g + (n >> 2)) * 64 + 2 * (kb2 * 16 + 4 * (n & 3));
+          const int aoff = (4 * g + (n >> 2)) * 64 + 16 * (n & 3) + 8 * kb2;
           const short4_t ads = lds_read_tr16(s_dst + aoff);
           const short4_t ap = lds_read_tr16(s_pt + aoff);
           const uint8_t* bq = s_q + (4 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
@@ -312,7 +356,7 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
         } else {
           // 16x16x32 over heads 8g .. 8g+7: two transposed reads per operand
           // (heads 8g + n/4 and 8g + 4 + n/4)
-          const int aoff = (8 * g + (n >> 2)) * 64 + 2 * (kb2 * 16 + 4 * (n & 3));
+          const int aoff = (8 * g + (n >> 2)) * 64 + 16 * (n & 3) + 8 * kb2;
           const bf16x8_t ads = join4(lds_read_tr16(s_dst + aoff), lds_read_tr16(s_dst + aoff + 4 * 64));
           const bf16x8_t ap = join4(lds_read_tr16(s_pt + aoff), lds_read_tr16(s_pt + aoff + 4 * 64));
           const uint8_t* bq = s_q + (8 * g + (n >> 2)) * kBwPitch + 8 * (n & 3);
@@ -342,7 +386,7 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
   for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
-      const int d = 16 * (9 * wave + k) + n;
+      const int d = 16 * (4 * k + wave) + n;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int h = h0 + 16 * ht + 4 * g + e;

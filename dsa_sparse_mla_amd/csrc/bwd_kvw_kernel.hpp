@@ -33,8 +33,8 @@
 //
 // LDS per step buffer: q latent [32 heads][1024 B], q rope [32][128 B],
 // dO [32][1024 B], then LSE and D [2][32] fp32: 69888 B, two buffers.
-// Granule G (16 B) of latent/dO row h sits at G ^ kw_swz(h) (within its
-// 256-byte group), rope granule G at G ^ kw_swz_r(h), so that the A-operand
+// Granule G (16 B) of latent/dO row h sits at G ^ bw_swz(h) (within its
+// 256-byte group), rope granule G at G ^ bw_swz_r(h), so that the A-operand
 // reads (16 rows at one granule) and the transposed reads (8 rows x 32 B
 // per half-wave) are free of bank conflicts.
 //
@@ -70,14 +70,6 @@ __device__ __forceinline__ float4_t kw_f4(const kw_lds* p) {
 __device__ __forceinline__ short4_t kw_tr(const kw_lds* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)p);
 }
-
-// Chosen by measurement (SQ_LDS_BANK_CONFLICT on probes of both read
-// patterns): the transposed reads need (swizzle >> 1) distinct over rows
-// 0..7 and over 8..15; the A-operand reads (16 rows at one logical
-// granule) are conflict-free with these and, e.g., with the identity, but
-// not with every XOR that is a bijection on 16 rows.
-__host__ __device__ constexpr int kw_swz(int h) { return (h & 6) | ((h & 1) << 3); }
-__host__ __device__ constexpr int kw_swz_r(int h) { return h & 6; }
 
 // One wave-wide 4-byte-per-lane copy HBM -> LDS: lane L's dword lands at LDS
 // byte lds_base + 4 * L (lds_base wave-uniform, in M0).
@@ -175,7 +167,7 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
   // group's last head.
   uint32_t cp_off[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cp_off[j] = 16u * (uint32_t)(lane ^ kw_swz(wave + 4 * j));
+  for (int j = 0; j < 4; ++j) cp_off[j] = 16u * (uint32_t)(lane ^ bw_swz(wave + 4 * j));
   const int64_t q_sh2 = 2 * q_sh, do_sh2 = 2 * do_sh;   // bytes
   struct CopyPlan {
     uint64_t qb, db;       // byte addresses of the step's token, head h0
@@ -204,7 +196,7 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
     } else if (k == 16) {
       const int h = 8 * wave + (lane >> 3);
       const int hq = c.h0 + min(h, c.hmax);
-      dma_16b(c.qt + hq * q_sh + kDv + 8 * ((lane & 7) ^ kw_swz_r(h)), c.bb + kKwQR + 8 * wave * 128);
+      dma_16b(c.qt + hq * q_sh + kDv + 8 * ((lane & 7) ^ bw_swz_r(h)), c.bb + kKwQR + 8 * wave * 128);
     } else if (wave == 0) {
       const int hq = c.h0 + min(lane & 31, c.hmax);
       dma_4b(lane < 32 ? lse_ptr + c.tok * lse_st + hq : d_ptr + c.tok * d_st + hq, c.bb + kKwLD);
@@ -229,14 +221,14 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
   {
     const int hr = 4 * g + (n >> 2), hb = (n >> 1) & 1;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) a_lat[c] = (uint32_t)(n * 1024 + 16 * ((4 * c + g) ^ kw_swz(n)));
-    a_rope = (uint32_t)(kKwQR + n * 128 + 16 * ((4 * ch + g) ^ kw_swz_r(n)));
+    for (int c = 0; c < 4; ++c) a_lat[c] = (uint32_t)(n * 1024 + 16 * ((4 * c + g) ^ bw_swz(n)));
+    a_rope = (uint32_t)(kKwQR + n * 128 + 16 * ((4 * ch + g) ^ bw_swz_r(n)));
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      t_lat[k] = (uint32_t)(hr * 1024 + 16 * ((2 * k + hb) ^ kw_swz(hr)) + 8 * (n & 1));
+      t_lat[k] = (uint32_t)(hr * 1024 + 16 * ((2 * k + hb) ^ bw_swz(hr)) + 8 * (n & 1));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      t_rope[i] = (uint32_t)(kKwQR + hr * 128 + 16 * ((2 * (2 * ch + i) + hb) ^ kw_swz_r(hr)) + 8 * (n & 1));
+      t_rope[i] = (uint32_t)(kKwQR + hr * 128 + 16 * ((2 * (2 * ch + i) + hb) ^ bw_swz_r(hr)) + 8 * (n & 1));
   }
   // exchange area of the pair: region X[w] is wave w's 4 KB
   const kw_lds* const xr_own = (const kw_lds*)&s_x[wave][0];

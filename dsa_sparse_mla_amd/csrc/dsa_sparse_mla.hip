@@ -17,6 +17,7 @@
 #include "fwd_kernel_ws.hpp"
 #include "bwd_kernel.hpp"
 #include "bwd_kvw_kernel.hpp"
+#include "bwd_dq_kernel.hpp"
 #include "topk_kernel.hpp"
 
 namespace {
@@ -603,7 +604,7 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
       hipLaunchKernelGGL(dsa::sparse_mla_bwd_kvw_kernel, kv_grid, dim3(256), 0, s, a, m);
       a.only = m.dup;
       a.only_nonzero = 0;
-      hipLaunchKernelGGL((dsa::sparse_mla_bwd_kernel<2, false>), dim3((unsigned)wgs), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(dsa::sparse_mla_bwd_dq_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a, m);
       a.only_nonzero = 1;
       hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, s, a);
     } else {

@@ -50,8 +50,7 @@ def test_source_hash_per_op(tmp_path, monkeypatch):
     change to the backward's kernel leaves the forward's hash alone."""
     csrc = tmp_path / "dsa_sparse_mla_amd" / "csrc"
     csrc.mkdir(parents=True)
-    for name in ("dsa_sparse_mla.hip", "fwd_kernel.hpp", "fwd_kernel_ws.hpp", "bwd_kernel.hpp",
-                 "bwd_kvw_kernel.hpp", "topk_kernel.hpp"):
+    for name in sorted(set().union(*bench.OP_SOURCES.values())):
         (csrc / name).write_text(name)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     before = {op: bench.source_hash(op) for op in ("fwd", "bwd", "topk")}
@@ -173,7 +172,7 @@ def test_counter_summary_per_kernel(tmp_path):
         w.writeheader()
         for disp, k, busy, mfma in ((1, "dsa::dkv_zero_kernel(float*, long, long)", 3200, 0),
                                     (2, "dsa::sparse_mla_bwd_kvw_kernel(dsa::BwdArgs, dsa::KvMajorArgs)", 320000, 2048000),
-                                    (3, "void dsa::sparse_mla_bwd_kernel<2, false>(dsa::BwdArgs)", 160000, 512000)):
+                                    (3, "dsa::sparse_mla_bwd_dq_kernel(dsa::BwdArgs, dsa::KvMajorArgs)", 160000, 512000)):
             w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "SQ_BUSY_CYCLES", "Counter_Value": busy})
             w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES",
                         "Counter_Value": mfma})
@@ -182,4 +181,4 @@ def test_counter_summary_per_kernel(tmp_path):
     out = json.load(open(tmp_path / "counters_bwd_wide.json"))
     assert "kvw" in out["kernel"] and out["mfma_busy_frac"] == 0.2   # 2048000 / (1024 * 320000 / 32)
     assert len(out["per_kernel"]) == 3
-    assert out["per_kernel"]["void dsa::sparse_mla_bwd_kernel<2, false>(dsa::BwdArgs)"]["mfma_busy_frac"] == 0.1
+    assert out["per_kernel"]["dsa::sparse_mla_bwd_dq_kernel(dsa::BwdArgs, dsa::KvMajorArgs)"]["mfma_busy_frac"] == 0.1
