@@ -89,7 +89,7 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
   __shared__ int s_tok[kKwChunk];
   __shared__ uint64_t s_msk[kKwChunk];
   __shared__ int s_wcnt[4];
-  __shared__ __attribute__((aligned(16))) uint8_t s_x[4][4096];   // the wave pairs' exchange area
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[4][2048];   // the wave pairs' exchange area
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -136,23 +136,23 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
   const float scale = a.scale, scale_log2 = a.scale_log2;
 
   // Waves pair up: wave (rh, ch) = (w >> 1, w & 1) owns rows r0 + 32rh ..
-  // +31 (two row tiles) and half ch of the columns: latent 256ch .. +255
-  // and rope 32ch .. +31 (nine 32-column chunks) for S^T, the latent half
-  // for dP^T, and the same 288 columns of dkv. Each q / dO operand read
-  // then feeds two MFMAs (one per row tile).
+  // +31 (two row tiles). It forms S^T and dP^T of its rows and head tile ch
+  // over all columns, and dkv of its rows on half ch of the columns (latent
+  // 256ch .. +255, rope 32ch .. +31). Each q / dO operand read feeds two
+  // MFMAs (one per row tile).
   const int rh = wave >> 1, ch = wave & 1;
 
   // ---- K rows as B operands: kreg[rt][j], lane (g, n) holds row 32rh + 16rt + n,
-  // columns 32 chunk(j) + 8g .. +7 (chunk j < 8: latent 8ch + j; j = 8: rope half ch)
-  bf16x8_t kreg[2][9];
+  // columns 32j + 8g .. +7 (chunks j < 16 latent, 16 and 17 rope)
+  bf16x8_t kreg[2][18];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const int64_t row = r0 + 32 * rh + 16 * rt + n;
     const bool ok = row < a.num_kv;
     const uint16_t* src = a.kv + (ok ? row : 0) * a.kv_st + 8 * g;
 #pragma unroll
-    for (int j = 0; j < 9; ++j) {
-      const bf16x8_t v = *(const bf16x8_t*)(src + (j < 8 ? 32 * (8 * ch + j) : kDv + 32 * ch));
+    for (int j = 0; j < 18; ++j) {
+      const bf16x8_t v = *(const bf16x8_t*)(src + 32 * j);
       kreg[rt][j] = ok ? v : (bf16x8_t){};
     }
   }
@@ -213,16 +213,18 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
     for (int k = 0; k < 18; ++k) acc[rt][k] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
   // Per-lane LDS offsets within a step buffer. A-operand reads of row
-  // 16ht + n: latent chunk 8ch + j at 256 ((8ch + j) >> 2) + a_lat[j & 3]
-  // (the XOR only touches a granule index's low 4 bits), the rope half at
-  // a_rope. Transposed reads of rows hr = 4g + n/4 and 16 + hr, latent column
-  // tile 16ch + k: 256 ((16ch + k) >> 3) + t_lat[k & 7]; rope tiles: t_rope[i].
-  uint32_t a_lat[4], a_rope, t_lat[8], t_rope[2];
+  // 16ch + n: latent chunk j at 256 (j >> 2) + a_lat[j & 3] (the XOR only
+  // touches a granule index's low 4 bits), rope chunk i at a_rope[i].
+  // Transposed reads of rows hr = 4g + n/4 and 16 + hr, latent column tile
+  // 16ch + k: 256 ((16ch + k) >> 3) + t_lat[k & 7]; rope tiles: t_rope[i].
+  uint32_t a_lat[4], a_rope[2], t_lat[8], t_rope[2];
   {
     const int hr = 4 * g + (n >> 2), hb = (n >> 1) & 1;
+    const int ar = 16 * ch + n;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) a_lat[c] = (uint32_t)(n * 1024 + 16 * ((4 * c + g) ^ bw_swz(n)));
-    a_rope = (uint32_t)(kKwQR + n * 128 + 16 * ((4 * ch + g) ^ bw_swz_r(n)));
+    for (int c = 0; c < 4; ++c) a_lat[c] = (uint32_t)(ar * 1024 + 16 * ((4 * c + g) ^ bw_swz(ar)));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a_rope[i] = (uint32_t)(kKwQR + ar * 128 + 16 * ((4 * i + g) ^ bw_swz_r(ar)));
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       t_lat[k] = (uint32_t)(hr * 1024 + 16 * ((2 * k + hb) ^ bw_swz(hr)) + 8 * (n & 1));
@@ -230,9 +232,8 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
     for (int i = 0; i < 2; ++i)
       t_rope[i] = (uint32_t)(kKwQR + hr * 128 + 16 * ((2 * (2 * ch + i) + hb) ^ bw_swz_r(hr)) + 8 * (n & 1));
   }
-  // exchange area of the pair: region X[w] is wave w's 4 KB
+  // exchange area of the pair: region X[w] is wave w's 2 KB
   const kw_lds* const xr_own = (const kw_lds*)&s_x[wave][0];
-  const kw_lds* const xr_pair = (const kw_lds*)&s_x[wave ^ 1][0];
   // The compiler does not see the asm copies' waits: make the K loads
   // complete here, with a wait it sees, so that it puts none in the loop
   // (there it would wait for the copies of the next step as well).
@@ -260,32 +261,29 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
     for (int c = 0; c < 4; ++c) pa[c] = buf + a_lat[c];
 #pragma unroll
     for (int k = 0; k < 8; ++k) pt[k] = buf + t_lat[k];
-    const kw_lds* const prope = buf + a_rope;
+    const kw_lds* const prope[2] = {buf + a_rope[0], buf + a_rope[1]};
     const int p = s / groups, hg = s - p * groups;
     const int h0 = kKwHeads * hg;
     const uint64_t msk = s_msk[p];
     const float4_t l4[2] = {kw_f4(buf + kKwLD + 16 * g), kw_f4(buf + kKwLD + 64 + 16 * g)};
     const float4_t d4[2] = {kw_f4(buf + kKwLD + 128 + 16 * g), kw_f4(buf + kKwLD + 192 + 16 * g)};
 
-    // ---- partial S^T and dP^T over the wave's columns: [head tile ht][row tile rt].
-    // 34 A-operand reads (q: chunks j = 0..8, dO: j = 0..7, both head
-    // tiles), each feeding two MFMAs, kRingA reads ahead; the order is
-    // pinned (the scheduler would sink each read next to its products).
-    // Read i: j = i / 4, head tile i & 1, q (i & 2 == 0) or dO; i = 32, 33:
-    // the rope chunk of head tile i & 1.
-    constexpr int kReadsA = 34, kRingA = 14;
+    // ---- S^T and dP^T of head tile ch over all columns: [row tile rt].
+    // 34 A-operand reads (q: chunks j = 0..17, dO: j = 0..15), each feeding
+    // two MFMAs, kRingA reads ahead; the order is pinned (the scheduler would
+    // sink each read next to its products). Read i < 32: chunk i / 2, q
+    // (i even) or dO (odd); i = 32, 33: the rope chunks of q.
+    constexpr int kReadsA = 34, kRingA = 12;
     auto a_read = [&](int i) -> bf16x8_t {
       if (i < 32) {
-        const int j = i >> 2, ht = i & 1, isdo = (i >> 1) & 1;
-        return kw_b128(pa[j & 3] + (isdo ? kKwDO : kKwQL) + 16 * 1024 * ht + 256 * ((8 * ch + j) >> 2));
+        const int j = i >> 1, isdo = i & 1;
+        return kw_b128(pa[j & 3] + (isdo ? kKwDO : kKwQL) + 256 * (j >> 2));
       }
-      return kw_b128(prope + 16 * 128 * (i & 1));
+      return kw_b128(prope[i - 32]);
     };
-    float4_t sacc[2][2], dacc[2][2];
+    float4_t sc[2], dc[2];
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) sacc[ht][rt] = dacc[ht][rt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < 2; ++rt) sc[rt] = dc[rt] = (float4_t){0.f, 0.f, 0.f, 0.f};
     bf16x8_t ra[kRingA];
 #pragma unroll
     for (int i = 0; i < kRingA; ++i) ra[i] = a_read(i);
@@ -295,34 +293,17 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
       if (i + kRingA < kReadsA) ra[i % kRingA] = a_read(i + kRingA);
       if ((i & 1) == 0) copy(cn, i >> 1);
       if (i == 1) copy(cn, 17);
-      const int j = i < 32 ? i >> 2 : 8;
-      const int ht = i & 1;
-      const bool isdo = i < 32 && ((i >> 1) & 1);
+      const int j = i < 32 ? i >> 1 : i - 16;
+      const bool isdo = i < 32 && (i & 1);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         if (isdo)
-          dacc[ht][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, kreg[rt][j], dacc[ht][rt], 0, 0, 0);
+          dc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, kreg[rt][j], dc[rt], 0, 0, 0);
         else
-          sacc[ht][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, kreg[rt][j], sacc[ht][rt], 0, 0, 0);
+          sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, kreg[rt][j], sc[rt], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-
-    // ---- the pair sums its partials: the wave keeps head tile ch and sends
-    // tile 1 - ch (S and dP of both row tiles: four float4 per lane)
-    {
-      float4_t* xo = (float4_t*)&s_x[wave][0];
-      xo[0 * 64 + lane] = sacc[1 - ch][0];
-      xo[1 * 64 + lane] = sacc[1 - ch][1];
-      xo[2 * 64 + lane] = dacc[1 - ch][0];
-      xo[3 * 64 + lane] = dacc[1 - ch][1];
-    }
-    __syncthreads();
-    float4_t sc[2], dc[2];
-    sc[0] = sacc[ch][0] + kw_f4(xr_pair + 16 * (0 * 64 + lane));
-    sc[1] = sacc[ch][1] + kw_f4(xr_pair + 16 * (1 * 64 + lane));
-    dc[0] = dacc[ch][0] + kw_f4(xr_pair + 16 * (2 * 64 + lane));
-    dc[1] = dacc[ch][1] + kw_f4(xr_pair + 16 * (3 * 64 + lane));
 
     // ---- transposed operands of the dkv product, kRingT column tiles ahead
     // (tile k < 16: q^T and dO^T, 4 reads; rope tiles k = 16, 17: q^T, 2)
@@ -363,8 +344,8 @@ sparse_mla_bwd_kvw_kernel(const BwdArgs a, const KvMajorArgs m) {
         own[rt][3] = pack_bf16x2(dsv[2], dsv[3]);
       }
     }
-    // ... and exchanges them: written to the region just read (the pair's),
-    // read from the wave's own (the pair writes there)
+    // ... and exchanges them through the pair's region (read from the
+    // wave's own, which the pair writes)
     {
       u32x4_t* xo = (u32x4_t*)&s_x[wave ^ 1][0];
       xo[0 * 64 + lane] = (u32x4_t){own[0][0], own[0][1], own[0][2], own[0][3]};
