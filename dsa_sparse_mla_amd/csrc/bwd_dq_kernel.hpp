@@ -66,14 +66,19 @@ __device__ __forceinline__ void dq_issue_tile(const BwdArgs& a, const uint32_t* 
           base + (uint32_t)(kBwLat + wave * 1024));
 }
 
+// s dS row swizzle (8-byte units; rows of 64 bytes)
+__device__ __forceinline__ constexpr int dst_swz(int n) { return (n & 6) | ((n >> 3) & 1); }
+
 // blockIdx.x = token * head_blocks + head block, over the tokens with
 // only[token] == 0 (only_nonzero = 0).
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
   constexpr int HT = 2;
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[kDqStages * kBwStage];
-  // s dS, bf16 [32 heads][32 keys]: bytes 16q .. 16q+7 of a head's row hold
-  // keys 4q .. 4q+3, bytes 16q+8 .. 16q+15 keys 16+4q .. 16+4q+3
+  // s dS, bf16 [32 heads][32 keys]: logical 8-byte unit 2q of a head's row
+  // holds keys 4q .. 4q+3, unit 2q+1 keys 16+4q .. 16+4q+3; unit u of head
+  // row h sits at u ^ dst_swz(h % 16), so that the 16 lanes a b64 write
+  // serves together hit distinct banks
   __shared__ __attribute__((aligned(16))) uint8_t s_dst[16 * HT * 64];
   __shared__ __attribute__((aligned(16))) uint32_t s_rows[kSegment];   // compacted row ids
   __shared__ int s_cnt[kChunks];
@@ -210,7 +215,7 @@ sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
           const float p = ok ? __builtin_amdgcn_exp2f(acc_s[e] * a.scale_log2 - l2) : 0.f;
           ds[e] = p * (acc_dp[e] - Dh) * a.scale;
         }
-        *(uint2*)(s_dst + (16 * ht + n) * 64 + 16 * g + 8 * kb) =
+        *(uint2*)(s_dst + (16 * ht + n) * 64 + 8 * ((2 * g + kb) ^ dst_swz(n))) =
             (uint2){pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
       }
       __syncthreads();
@@ -220,7 +225,11 @@ sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
       {
         bf16x8_t ads[HT];
 #pragma unroll
-        for (int t = 0; t < HT; ++t) ads[t] = lds16(s_dst + (16 * t + n) * 64 + 16 * g);
+        for (int t = 0; t < HT; ++t) {
+          // units 2g, 2g+1 share a granule; an odd swizzle stores them swapped
+          const bf16x8_t v = lds16(s_dst + (16 * t + n) * 64 + 16 * (g ^ (dst_swz(n) >> 1)));
+          ads[t] = (dst_swz(n) & 1) ? __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3) : v;
+        }
         constexpr int kRA = 4;
         bf16x8_t kb_ring[kRA];
         auto kt_read = [&](int k) {
