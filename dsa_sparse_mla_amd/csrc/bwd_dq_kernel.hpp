@@ -30,8 +30,9 @@
 
 namespace dsa {
 
+constexpr int kDqWaves = 8;                                   // 4 S waves, 4 dq waves: two per SIMD
 constexpr int kDqStages = 4;                                  // LDS ring depth
-constexpr int kDqDmaPerWave = kTileKeys / 4 + 1;              // 8 latent rows + 8 rope rows: 9 copies
+constexpr int kDqDmaPerWave = kTileKeys / 4 + 1;              // per dq wave: 8 latent rows + 8 rope rows, 9 copies
 static_assert(kBwStage % 1024 == 0, "stages keep the 1 KB copy alignment");
 
 // Copy tile t into stage t % kDqStages: wave w takes latent rows 8w .. 8w+7
@@ -71,89 +72,27 @@ __device__ __forceinline__ constexpr int dst_swz(int n) { return (n & 6) | ((n >
 
 // blockIdx.x = token * head_blocks + head block, over the tokens with
 // only[token] == 0 (only_nonzero = 0).
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(64 * kDqWaves)
 sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
   constexpr int HT = 2;
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[kDqStages * kBwStage];
-  // s dS, bf16 [32 heads][32 keys]: logical 8-byte unit 2q of a head's row
-  // holds keys 4q .. 4q+3, unit 2q+1 keys 16+4q .. 16+4q+3; unit u of head
-  // row h sits at u ^ dst_swz(h % 16), so that the 16 lanes a b64 write
-  // serves together hit distinct banks
-  __shared__ __attribute__((aligned(16))) uint8_t s_dst[16 * HT * 64];
+  // s dS, bf16 [32 heads][32 keys], one buffer per tile parity: logical
+  // 8-byte unit 2q of a head's row holds keys 4q .. 4q+3, unit 2q+1 keys
+  // 16+4q .. 16+4q+3; unit u of head row h sits at u ^ dst_swz(h % 16), so
+  // that the 16 lanes a b64 write serves together hit distinct banks
+  __shared__ __attribute__((aligned(16))) uint8_t s_dst[2][16 * HT * 64];
   __shared__ __attribute__((aligned(16))) uint32_t s_rows[kSegment];   // compacted row ids
   __shared__ int s_cnt[kChunks];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool is_s = wave < 4;   // role (uniform per wave)
+  const int sw = wave & 3;      // index within the role
   const int n = lane & 15, g = lane >> 4;   // MFMA column / k-group of the lane
   const int64_t token = blockIdx.x / a.head_blocks;
   const int h0 = (int)(blockIdx.x % a.head_blocks) * 16 * HT;
   if (a.only && ((a.only[token] != 0u) != (a.only_nonzero != 0))) return;   // uniform over the workgroup
-
-  // ---------------------------------------------------------------- per-token inputs
-  // Phases 1 and 2: key block kb, head tile ht; the lane's head is h0 + 16ht + n.
-  const int kb = wave & 1, ht = wave >> 1;
-  const int head = h0 + 16 * ht + n;
-  const bool head_ok = head < a.num_heads;
-  // Q^T and dO^T as the MFMA B operand: lane holds columns 32c + 8g .. +7 of its head
-  bf16x8_t bq[kDqk / 32], bdo[kDv / 32];
-  {
-    const int hh = head_ok ? head : 0;
-    const uint16_t* qp = a.q + token * a.q_st + (int64_t)hh * a.q_sh + 8 * g;
-    const uint16_t* dp = a.dout + token * a.do_st + (int64_t)hh * a.do_sh + 8 * g;
-#pragma unroll
-    for (int c = 0; c < kDqk / 32; ++c) {
-      const bf16x8_t v = *(const bf16x8_t*)(qp + 32 * c);
-      bq[c] = head_ok ? v : (bf16x8_t){};
-    }
-#pragma unroll
-    for (int c = 0; c < kDv / 32; ++c) {
-      const bf16x8_t v = *(const bf16x8_t*)(dp + 32 * c);
-      bdo[c] = head_ok ? v : (bf16x8_t){};
-    }
-  }
-  // D from the prepass; LSE in log2 units, +inf for padded heads (P = 0 there)
-  const float Dh = head_ok ? m.dbuf[token * m.d_st + head] : 0.f;
-  const float l2 = head_ok ? a.lse[token * a.lse_st + head] * 1.4426950408889634f : INFINITY;
-  // Use the loads here, so the compiler's waits for them sit before the
-  // loop; a wait at a first use inside it would also wait for later copies.
-#pragma unroll
-  for (int c = 0; c < kDqk / 32; ++c) asm volatile("" ::"v"(bq[c]));
-#pragma unroll
-  for (int c = 0; c < kDv / 32; ++c) asm volatile("" ::"v"(bdo[c]));
-  asm volatile("" ::"v"(Dh), "v"(l2));
-
-  // dq column tiles m = 4k + w (k = 0 .. 8) of head tile t: lane holds
-  // column 16m + n of heads 16t + 4g .. +3
-  float4_t dq_acc[HT][9];
-#pragma unroll
-  for (int t = 0; t < HT; ++t)
-#pragma unroll
-    for (int k = 0; k < 9; ++k) dq_acc[t][k] = (float4_t){0.f, 0.f, 0.f, 0.f};
-
-  // Stage offsets of the lane's reads. Phase 1 (A operand): key kb*16 + n,
-  // logical granule c' = 4c + g; latent c = 4i + c'' at a_lat[c''] + 256i,
-  // rope c = 16 + c'' at a_rope[c''].
-  uint32_t a_lat[4], a_rope[2];
-  {
-    const int r = kb * 16 + n;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) a_lat[c] = (uint32_t)(r * 1024 + 16 * ((4 * c + g) ^ bw_swz(r)));
-#pragma unroll
-    for (int c = 0; c < 2; ++c) a_rope[c] = (uint32_t)(kBwLat + r * 128 + 16 * ((4 * c + g) ^ bw_swz_r(r)));
-  }
-  // Phase 3 (K^T operand of column tile m = 4k + w): lane (g, n) points at
-  // key 4g + n/4 (and 16 + 4g + n/4), columns 16m + 4(n % 4) ..; latent tile
-  // k at t_lat[k % 2] + 256 (k / 2), the rope tile (k = 8) at t_rope.
-  uint32_t t_lat[2], t_rope;
-  {
-    const int r = 4 * g + (n >> 2), hb = (n >> 1) & 1;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      t_lat[i] = (uint32_t)(r * 1024 + 16 * ((2 * (wave + 4 * i) + hb) ^ bw_swz(r)) + 8 * (n & 1));
-    t_rope = (uint32_t)(kBwLat + r * 128 + 16 * ((2 * wave + hb) ^ bw_swz_r(r)) + 8 * (n & 1));
-  }
 
   FwdArgs fa = {};   // the forward's index stage, with row ids as the offsets
   fa.idx = a.idx;
@@ -163,117 +102,185 @@ sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
   fa.topk = a.topk;
   fa.seg_len = kSegment;
   const uint32_t stage_lds = lds_offset(s_stage);
-
   const int nseg = (a.topk + kSegment - 1) / kSegment;
-  for (int seg = 0; seg < nseg; ++seg) {
-    const int nvalid = build_key_list<false>(fa, token, seg, wave, lane, s_rows, s_cnt, [] {});
-    const int ntiles = (nvalid + kTileKeys - 1) / kTileKeys;
-    if (ntiles == 0) continue;   // uniform
 
-    dq_issue_tile(a, s_rows, stage_lds, 0, wave, lane);
-    if (ntiles > 1) dq_issue_tile(a, s_rows, stage_lds, 1, wave, lane);
-    if (ntiles > 2) dq_issue_tile(a, s_rows, stage_lds, 2, wave, lane);
-    if (ntiles > 2) wait_vmem<2 * kDqDmaPerWave>();
-    else if (ntiles > 1) wait_vmem<kDqDmaPerWave>();
-    else wait_vmem<0>();
-    __syncthreads();
-
-    for (int j = 0; j < ntiles; ++j) {
-      // stage (j + 3) % 4 held tile j - 1: every wave left it at the last barrier
-      if (j + 3 < ntiles) dq_issue_tile(a, s_rows, stage_lds, j + 3, wave, lane);
-      const uint8_t* st = s_stage + (j % kDqStages) * kBwStage;
-
-      // ---- phase 1: S^T and dP^T of key block kb, head tile ht
-      float4_t acc_s = {0.f, 0.f, 0.f, 0.f}, acc_dp = {0.f, 0.f, 0.f, 0.f};
-      {
-        auto a_read = [&](int c) {
-          return lds16(c < 16 ? st + a_lat[c & 3] + 256 * (c >> 2) : st + a_rope[c - 16]);
-        };
-        // A operands read 6 ahead (pinned order: the scheduler would
-        // otherwise sink each read next to its products)
-        constexpr int kRing = 6;
-        bf16x8_t ring[kRing];
+  // Barrier sequence per index segment, every wave: the index stage's two;
+  // tile 0 landed; then after iteration j < ntiles: s dS of tile j written
+  // and tile j+1 landed. In iteration j the S waves form s dS of tile j and
+  // the dq waves take the dq products of tile j - 1 and copy tile j + 2
+  // into the stage of tile j - 2.
+  if (is_s) {
+    // ============================================================ S waves
+    // Key block kb, head tile ht; the lane's head is h0 + 16ht + n.
+    const int kb = sw & 1, ht = sw >> 1;
+    const int head = h0 + 16 * ht + n;
+    const bool head_ok = head < a.num_heads;
+    // Q^T and dO^T as the MFMA B operand: lane holds columns 32c + 8g .. +7 of its head
+    bf16x8_t bq[kDqk / 32], bdo[kDv / 32];
+    {
+      const int hh = head_ok ? head : 0;
+      const uint16_t* qp = a.q + token * a.q_st + (int64_t)hh * a.q_sh + 8 * g;
+      const uint16_t* dp = a.dout + token * a.do_st + (int64_t)hh * a.do_sh + 8 * g;
 #pragma unroll
-        for (int c = 0; c < kRing; ++c) ring[c] = a_read(c);
-#pragma unroll
-        for (int c = 0; c < kDqk / 32; ++c) {
-          const bf16x8_t av = ring[c % kRing];
-          if (c + kRing < kDqk / 32) ring[c % kRing] = a_read(c + kRing);
-          acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[c], acc_s, 0, 0, 0);
-          if (c < kDv / 32) acc_dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bdo[c], acc_dp, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int c = 0; c < kDqk / 32; ++c) {
+        const bf16x8_t v = *(const bf16x8_t*)(qp + 32 * c);
+        bq[c] = head_ok ? v : (bf16x8_t){};
       }
+#pragma unroll
+      for (int c = 0; c < kDv / 32; ++c) {
+        const bf16x8_t v = *(const bf16x8_t*)(dp + 32 * c);
+        bdo[c] = head_ok ? v : (bf16x8_t){};
+      }
+    }
+    // D from the prepass; LSE in log2 units, +inf for padded heads (P = 0 there)
+    const float Dh = head_ok ? m.dbuf[token * m.d_st + head] : 0.f;
+    const float l2 = head_ok ? a.lse[token * a.lse_st + head] * 1.4426950408889634f : INFINITY;
+    // A-operand offsets: key kb*16 + n, logical granule c' = 4c + g; latent
+    // c = 4i + c'' at a_lat[c''] + 256i, rope c = 16 + c'' at a_rope[c''].
+    uint32_t a_lat[4], a_rope[2];
+    {
+      const int r = kb * 16 + n;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a_lat[c] = (uint32_t)(r * 1024 + 16 * ((4 * c + g) ^ bw_swz(r)));
+#pragma unroll
+      for (int c = 0; c < 2; ++c) a_rope[c] = (uint32_t)(kBwLat + r * 128 + 16 * ((4 * c + g) ^ bw_swz_r(r)));
+    }
 
-      // ---- phase 2: P and s*dS (lane: head 16ht + n, keys kb*16 + 4g + e)
-      {
-        const int lim = nvalid - j * kTileKeys;
-        float ds[4];
+    for (int seg = 0; seg < nseg; ++seg) {
+      const int nvalid = build_key_list<false, kDqWaves>(fa, token, seg, wave, lane, s_rows, s_cnt, [] {});
+      const int ntiles = (nvalid + kTileKeys - 1) / kTileKeys;
+      if (ntiles == 0) continue;   // uniform
+      __syncthreads();             // tile 0 landed
+      for (int j = 0; j < ntiles; ++j) {
+        const uint8_t* st = s_stage + (j % kDqStages) * kBwStage;
+        // ---- phase 1: S^T and dP^T of key block kb, head tile ht
+        float4_t acc_s = {0.f, 0.f, 0.f, 0.f}, acc_dp = {0.f, 0.f, 0.f, 0.f};
+        {
+          auto a_read = [&](int c) {
+            return lds16(c < 16 ? st + a_lat[c & 3] + 256 * (c >> 2) : st + a_rope[c - 16]);
+          };
+          // A operands read 6 ahead (pinned order: the scheduler would
+          // otherwise sink each read next to its products)
+          constexpr int kRing = 6;
+          bf16x8_t ring[kRing];
+#pragma unroll
+          for (int c = 0; c < kRing; ++c) ring[c] = a_read(c);
+#pragma unroll
+          for (int c = 0; c < kDqk / 32; ++c) {
+            const bf16x8_t av = ring[c % kRing];
+            if (c + kRing < kDqk / 32) ring[c % kRing] = a_read(c + kRing);
+            acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[c], acc_s, 0, 0, 0);
+            if (c < kDv / 32) acc_dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bdo[c], acc_dp, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // ---- phase 2: P and s*dS (lane: head 16ht + n, keys kb*16 + 4g + e)
+        {
+          const int lim = nvalid - j * kTileKeys;
+          float ds[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool ok = kb * 16 + 4 * g + e < lim;
+            const float p = ok ? __builtin_amdgcn_exp2f(acc_s[e] * a.scale_log2 - l2) : 0.f;
+            ds[e] = p * (acc_dp[e] - Dh) * a.scale;
+          }
+          *(uint2*)(s_dst[j & 1] + (16 * ht + n) * 64 + 8 * ((2 * g + kb) ^ dst_swz(n))) =
+              (uint2){pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
+        }
+        __syncthreads();   // s dS of tile j written; tile j+1 landed
+      }
+    }
+  } else {
+    // ============================================================ dq waves
+    // dq column tiles m = 4k + sw (k = 0 .. 8) of head tile t: lane holds
+    // column 16m + n of heads 16t + 4g .. +3
+    float4_t dq_acc[HT][9];
+#pragma unroll
+    for (int t = 0; t < HT; ++t)
+#pragma unroll
+      for (int k = 0; k < 9; ++k) dq_acc[t][k] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    // K^T operand of column tile m = 4k + sw: lane (g, n) points at key
+    // 4g + n/4 (and 16 + 4g + n/4), columns 16m + 4(n % 4) ..; latent tile
+    // k at t_lat[k % 2] + 256 (k / 2), the rope tile (k = 8) at t_rope.
+    uint32_t t_lat[2], t_rope;
+    {
+      const int r = 4 * g + (n >> 2), hb = (n >> 1) & 1;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        t_lat[i] = (uint32_t)(r * 1024 + 16 * ((2 * (sw + 4 * i) + hb) ^ bw_swz(r)) + 8 * (n & 1));
+      t_rope = (uint32_t)(kBwLat + r * 128 + 16 * ((2 * sw + hb) ^ bw_swz_r(r)) + 8 * (n & 1));
+    }
+    // ---- phase 3 of tile j: dq tiles 4k + sw += (s dS)[16 heads x 32 keys] K[32 keys x 16 columns],
+    //      k slots 8g .. 8g+7 = keys 4g .. 4g+3, 16+4g .. 16+4g+3
+    auto phase3 = [&](int j) {
+      const uint8_t* st = s_stage + (j % kDqStages) * kBwStage;
+      bf16x8_t ads[HT];
+#pragma unroll
+      for (int t = 0; t < HT; ++t) {
+        // units 2g, 2g+1 share a granule; an odd swizzle stores them swapped
+        const bf16x8_t v = lds16(s_dst[j & 1] + (16 * t + n) * 64 + 16 * (g ^ (dst_swz(n) >> 1)));
+        ads[t] = (dst_swz(n) & 1) ? __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3) : v;
+      }
+      constexpr int kRA = 4;
+      bf16x8_t kb_ring[kRA];
+      auto kt_read = [&](int k) {
+        if (k < 8) {
+          const uint8_t* p = st + t_lat[k & 1] + 256 * (k >> 1);
+          return join4(lds_read_tr16(p), lds_read_tr16(p + 16 * 1024));
+        }
+        const uint8_t* p = st + t_rope;
+        return join4(lds_read_tr16(p), lds_read_tr16(p + 16 * 128));
+      };
+#pragma unroll
+      for (int k = 0; k < kRA; ++k) kb_ring[k] = kt_read(k);
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        const bf16x8_t b = kb_ring[k % kRA];
+        if (k + kRA < 9) kb_ring[k % kRA] = kt_read(k + kRA);
+#pragma unroll
+        for (int t = 0; t < HT; ++t)
+          dq_acc[t][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads[t], b, dq_acc[t][k], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    for (int seg = 0; seg < nseg; ++seg) {
+      const int nvalid = build_key_list<false, kDqWaves>(fa, token, seg, wave, lane, s_rows, s_cnt, [] {});
+      const int ntiles = (nvalid + kTileKeys - 1) / kTileKeys;
+      if (ntiles == 0) continue;   // uniform
+      dq_issue_tile(a, s_rows, stage_lds, 0, sw, lane);
+      if (ntiles > 1) {
+        dq_issue_tile(a, s_rows, stage_lds, 1, sw, lane);
+        wait_vmem<kDqDmaPerWave>();
+      } else {
+        wait_vmem<0>();
+      }
+      __syncthreads();   // tile 0 landed
+      for (int j = 0; j < ntiles; ++j) {
+        // stage (j + 2) % 4 held tile j - 2: every wave left it at the last barrier
+        if (j + 2 < ntiles) dq_issue_tile(a, s_rows, stage_lds, j + 2, sw, lane);
+        if (j > 0) phase3(j - 1);
+        // tile j+1 landed in this wave (tile j+2 may still fly)
+        if (j + 2 < ntiles) wait_vmem<kDqDmaPerWave>();
+        else wait_vmem<0>();
+        __syncthreads();   // s dS of tile j written; tile j+1 landed
+      }
+      phase3(ntiles - 1);
+    }
+
+    // ---------------------------------------------------------------- dq (fp32)
+#pragma unroll
+    for (int t = 0; t < HT; ++t)
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        const int d = 16 * (4 * k + sw) + n;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool ok = kb * 16 + 4 * g + e < lim;
-          const float p = ok ? __builtin_amdgcn_exp2f(acc_s[e] * a.scale_log2 - l2) : 0.f;
-          ds[e] = p * (acc_dp[e] - Dh) * a.scale;
-        }
-        *(uint2*)(s_dst + (16 * ht + n) * 64 + 8 * ((2 * g + kb) ^ dst_swz(n))) =
-            (uint2){pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
-      }
-      __syncthreads();
-
-      // ---- phase 3: dq tiles 4k + w += (s dS)[16 heads x 32 keys] K[32 keys x 16 columns],
-      //      k slots 8g .. 8g+7 = keys 4g .. 4g+3, 16+4g .. 16+4g+3
-      {
-        bf16x8_t ads[HT];
-#pragma unroll
-        for (int t = 0; t < HT; ++t) {
-          // units 2g, 2g+1 share a granule; an odd swizzle stores them swapped
-          const bf16x8_t v = lds16(s_dst + (16 * t + n) * 64 + 16 * (g ^ (dst_swz(n) >> 1)));
-          ads[t] = (dst_swz(n) & 1) ? __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3) : v;
-        }
-        constexpr int kRA = 4;
-        bf16x8_t kb_ring[kRA];
-        auto kt_read = [&](int k) {
-          if (k < 8) {
-            const uint8_t* p = st + t_lat[k & 1] + 256 * (k >> 1);
-            return join4(lds_read_tr16(p), lds_read_tr16(p + 16 * 1024));
-          }
-          const uint8_t* p = st + t_rope;
-          return join4(lds_read_tr16(p), lds_read_tr16(p + 16 * 128));
-        };
-#pragma unroll
-        for (int k = 0; k < kRA; ++k) kb_ring[k] = kt_read(k);
-#pragma unroll
-        for (int k = 0; k < 9; ++k) {
-          const bf16x8_t b = kb_ring[k % kRA];
-          if (k + kRA < 9) kb_ring[k % kRA] = kt_read(k + kRA);
-#pragma unroll
-          for (int t = 0; t < HT; ++t)
-            dq_acc[t][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ads[t], b, dq_acc[t][k], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+          const int h = h0 + 16 * t + 4 * g + e;
+          if (h < a.num_heads) a.dq[token * a.dq_st + (int64_t)h * a.dq_sh + d] = dq_acc[t][k][e];
         }
       }
-      if (j + 1 < ntiles) {
-        // tile j+1 landed in this wave (later tiles may still fly), then in every wave
-        if (j + 3 < ntiles) wait_vmem<2 * kDqDmaPerWave>();
-        else if (j + 2 < ntiles) wait_vmem<kDqDmaPerWave>();
-        else wait_vmem<0>();
-        __syncthreads();
-      }
-    }
   }
-
-  // ---------------------------------------------------------------- dq (fp32)
-#pragma unroll
-  for (int t = 0; t < HT; ++t)
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      const int d = 16 * (4 * k + wave) + n;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int h = h0 + 16 * t + 4 * g + e;
-        if (h < a.num_heads) a.dq[token * a.dq_st + (int64_t)h * a.dq_sh + d] = dq_acc[t][k][e];
-      }
-    }
 }
 
 }  // namespace dsa

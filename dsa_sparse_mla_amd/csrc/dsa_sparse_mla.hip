@@ -604,7 +604,7 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
       hipLaunchKernelGGL(dsa::sparse_mla_bwd_kvw_kernel, kv_grid, dim3(256), 0, s, a, m);
       a.only = m.dup;
       a.only_nonzero = 0;
-      hipLaunchKernelGGL(dsa::sparse_mla_bwd_dq_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a, m);
+      hipLaunchKernelGGL(dsa::sparse_mla_bwd_dq_kernel, dim3((unsigned)wgs), dim3(64 * dsa::kDqWaves), 0, s, a, m);
       a.only_nonzero = 1;
       hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, s, a);
     } else {
