@@ -18,8 +18,9 @@
 //      the next byte. After four passes the k-th key K is known, and so is how
 //      many keys equal to K are taken (the first ones by column).
 //   2. one ordered pass: key > K, or key == K among the first of them, is
-//      selected; a workgroup-wide prefix count over 512-column chunks gives
-//      each selected column its place, so the row comes out ascending.
+//      selected; workgroup-wide prefix counts over 4096-column chunks (8
+//      consecutive columns per thread) give each selected column its place,
+//      so the row comes out ascending.
 // A row with at most topk candidates skips all of this and is written as its
 // whole range (no score is read).
 //
@@ -49,6 +50,9 @@ struct TopkArgs {
 constexpr int kTkThreads = 512;
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kTkCache = 16384;   // candidate keys held in LDS (64 KB)
+constexpr int kTkPer = 8;         // consecutive columns per thread in a chunk
+constexpr int kTkChunk = kTkThreads * kTkPer;   // columns per chunk (4096)
+static_assert(kTkCache % kTkChunk == 0, "cached rows end on a chunk boundary");
 
 // Unsigned order of the result = selection order of the scores: NaN -> 0
 // (below -inf, whose key is 0x007fffff), -0 -> +0, negatives reversed below
@@ -91,7 +95,21 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
 
   const float* srow = a.scores + t * a.score_st + lo;
   const bool cached = n <= kTkCache;
-  auto key_at = [&](int64_t j) -> uint32_t { return cached ? s_key[j] : score_key(srow[j]); };
+  // kTkPer keys j0 + i * stride (i < kTkPer), read without branches: indices
+  // past the row are clamped to its last column (the caller masks them), so
+  // the loads are issued together
+  auto load_keys = [&](bool from_lds, int64_t j0, int64_t stride, uint32_t* key) {
+    if (from_lds) {
+#pragma unroll
+      for (int i = 0; i < kTkPer; ++i) key[i] = s_key[min(j0 + i * stride, n - 1)];
+    } else {
+      float f[kTkPer];
+#pragma unroll
+      for (int i = 0; i < kTkPer; ++i) f[i] = srow[min(j0 + i * stride, n - 1)];
+#pragma unroll
+      for (int i = 0; i < kTkPer; ++i) key[i] = score_key(f[i]);
+    }
+  };
 
   // ---------------------------------------------------------------- 1. radix select
   uint32_t prefix = 0, mask = 0;
@@ -100,16 +118,18 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < kTkWaves * 256; i += kTkThreads) (&s_hist[0][0])[i] = 0u;
     __syncthreads();
-    if (pass == 0) {
-      for (int64_t j = tid; j < n; j += kTkThreads) {
-        const uint32_t key = score_key(srow[j]);
-        if (cached) s_key[j] = key;
-        atomicAdd(&s_hist[wave][key >> 24], 1u);
-      }
-    } else {
-      for (int64_t j = tid; j < n; j += kTkThreads) {
-        const uint32_t key = key_at(j);
-        if (((key ^ prefix) & mask) == 0u) atomicAdd(&s_hist[wave][(key >> shift) & 255u], 1u);
+    // kTkPer keys per thread and round
+    const bool from_lds = pass > 0 && cached;
+    for (int64_t j0 = tid; j0 < n; j0 += (int64_t)kTkThreads * kTkPer) {
+      uint32_t key[kTkPer];
+      load_keys(from_lds, j0, kTkThreads, key);
+#pragma unroll
+      for (int i = 0; i < kTkPer; ++i) {
+        const int64_t j = j0 + (int64_t)i * kTkThreads;
+        if (j < n) {
+          if (pass == 0 && cached) s_key[j] = key[i];
+          if (((key[i] ^ prefix) & mask) == 0u) atomicAdd(&s_hist[wave][(key[i] >> shift) & 255u], 1u);
+        }
       }
     }
     __syncthreads();
@@ -147,39 +167,64 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
   const uint32_t K = prefix;    // the k-th key; `remaining` keys equal to it are taken
 
   // ---------------------------------------------------------------- 2. ordered compaction
+  // Chunks of kTkChunk columns; thread tid takes columns kTkPer tid .. +kTkPer-1
+  // of the chunk, so thread order is column order. Two workgroup prefix
+  // counts per chunk: the keys equal to K before each column, then the
+  // selected columns before each. The next chunk's keys are loaded first.
+  // Exclusive prefix of v over the threads and its total (s_wsum[buf]).
+  auto wg_scan = [&](uint32_t v, int buf, uint32_t& total) -> uint32_t {
+    uint32_t incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_wsum[buf][wave] = incl;
+    __syncthreads();
+    uint32_t before = incl - v;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) {
+      const uint32_t x = s_wsum[buf][w];
+      before += w < wave ? x : 0u;
+      total += x;
+    }
+    return before;
+  };
+  auto load_chunk = [&](int64_t c0, uint32_t* key) { load_keys(cached, c0 + (int64_t)kTkPer * tid, 1, key); };
   uint32_t eq_base = 0, sel_base = 0;
-  int par = 0;
-  for (int64_t c0 = 0; c0 < n; c0 += kTkThreads, par ^= 1) {
-    const int64_t j = c0 + tid;
-    const uint32_t key = j < n ? key_at(j) : 0u;
-    const bool in = j < n;
-    const bool gt = in && key > K;
-    const bool eq = in && key == K;
-    const uint64_t eqm = __ballot(eq);
-    if (lane == 0) s_wsum[par][wave] = (uint32_t)__builtin_popcountll(eqm);
-    __syncthreads();
-    uint32_t eq_before = eq_base + lanes_below(eqm), eq_all = 0;
+  uint32_t cur[kTkPer], nxt[kTkPer];
+  load_chunk(0, cur);
+  for (int64_t c0 = 0; c0 < n && sel_base < (uint32_t)k; c0 += kTkChunk) {
+    if (c0 + kTkChunk < n) load_chunk(c0 + kTkChunk, nxt);
+    const int64_t jt = c0 + (int64_t)kTkPer * tid;   // this thread's first column
+    uint32_t neq = 0;
 #pragma unroll
-    for (int w = 0; w < kTkWaves; ++w) {
-      const uint32_t v = s_wsum[par][w];
-      eq_before += w < wave ? v : 0u;
-      eq_all += v;
-    }
-    const bool sel = gt || (eq && eq_before < remaining);
-    const uint64_t selm = __ballot(sel);
-    __syncthreads();   // every wave has read s_wsum[par]
-    if (lane == 0) s_wsum[par][wave] = (uint32_t)__builtin_popcountll(selm);
-    __syncthreads();
-    uint32_t pos = sel_base + lanes_below(selm), sel_all = 0;
+    for (int i = 0; i < kTkPer; ++i) neq += (jt + i < n && cur[i] == K) ? 1u : 0u;
+    uint32_t eq_all, sel_all;
+    uint32_t e = eq_base + wg_scan(neq, 0, eq_all);
+    bool sel[kTkPer];
+    uint32_t nsel = 0;
 #pragma unroll
-    for (int w = 0; w < kTkWaves; ++w) {
-      const uint32_t v = s_wsum[par][w];
-      pos += w < wave ? v : 0u;
-      sel_all += v;
+    for (int i = 0; i < kTkPer; ++i) {
+      const bool in = jt + i < n;
+      const bool eq = in && cur[i] == K;
+      sel[i] = (in && cur[i] > K) || (eq && e < remaining);
+      e += eq ? 1u : 0u;
+      nsel += sel[i] ? 1u : 0u;
     }
-    if (sel && pos < (uint32_t)k) orow[pos] = (int32_t)(lo + j);   // exactly k are selected
+    uint32_t pos = sel_base + wg_scan(nsel, 1, sel_all);
+#pragma unroll
+    for (int i = 0; i < kTkPer; ++i) {
+      if (sel[i]) {
+        if (pos < (uint32_t)k) orow[pos] = (int32_t)(lo + jt + i);   // exactly k are selected
+        ++pos;
+      }
+    }
     eq_base += eq_all;
     sel_base += sel_all;
+#pragma unroll
+    for (int i = 0; i < kTkPer; ++i) cur[i] = nxt[i];
   }
 }
 
