@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 namespace dsa {
 
@@ -95,20 +96,23 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
 
   const float* srow = a.scores + t * a.score_st + lo;
   const bool cached = n <= kTkCache;
-  // kTkPer keys j0 + i * stride (i < kTkPer), read without branches: indices
-  // past the row are clamped to its last column (the caller masks them), so
-  // the loads are issued together
-  auto load_keys = [&](bool from_lds, int64_t j0, int64_t stride, uint32_t* key) {
-    if (from_lds) {
+  // kTkPer entries j0 + i * stride (i < kTkPer), read without branches:
+  // indices past the row are clamped to its last column (the caller masks
+  // them), so the loads are issued together. From LDS they are keys; from
+  // the scores, raw score bits that to_key turns into keys when used.
+  auto load_raw = [&](auto lds_tag, int64_t j0, int64_t stride, uint32_t* raw) {
+    if constexpr (decltype(lds_tag)::value) {
 #pragma unroll
-      for (int i = 0; i < kTkPer; ++i) key[i] = s_key[min(j0 + i * stride, n - 1)];
+      for (int i = 0; i < kTkPer; ++i) raw[i] = s_key[min(j0 + i * stride, n - 1)];
     } else {
-      float f[kTkPer];
+      const uint32_t* sr = reinterpret_cast<const uint32_t*>(srow);
 #pragma unroll
-      for (int i = 0; i < kTkPer; ++i) f[i] = srow[min(j0 + i * stride, n - 1)];
-#pragma unroll
-      for (int i = 0; i < kTkPer; ++i) key[i] = score_key(f[i]);
+      for (int i = 0; i < kTkPer; ++i) raw[i] = sr[min(j0 + i * stride, n - 1)];
     }
+  };
+  auto to_key = [](auto lds_tag, uint32_t raw) {
+    if constexpr (decltype(lds_tag)::value) return raw;
+    else return score_key(__uint_as_float(raw));
   };
 
   // ---------------------------------------------------------------- 1. radix select
@@ -118,20 +122,29 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < kTkWaves * 256; i += kTkThreads) (&s_hist[0][0])[i] = 0u;
     __syncthreads();
-    // kTkPer keys per thread and round
-    const bool from_lds = pass > 0 && cached;
-    for (int64_t j0 = tid; j0 < n; j0 += (int64_t)kTkThreads * kTkPer) {
-      uint32_t key[kTkPer];
-      load_keys(from_lds, j0, kTkThreads, key);
+    // kTkPer keys per thread and round; the next round's entries are
+    // loaded before this round's are counted (one loop per source)
+    auto count = [&](auto lds_tag) {
+      constexpr int64_t kRound = (int64_t)kTkThreads * kTkPer;
+      uint32_t nxt[kTkPer];
+      load_raw(lds_tag, tid, kTkThreads, nxt);
+      for (int64_t j0 = tid; j0 < n; j0 += kRound) {
+        uint32_t key[kTkPer];
 #pragma unroll
-      for (int i = 0; i < kTkPer; ++i) {
-        const int64_t j = j0 + (int64_t)i * kTkThreads;
-        if (j < n) {
-          if (pass == 0 && cached) s_key[j] = key[i];
-          if (((key[i] ^ prefix) & mask) == 0u) atomicAdd(&s_hist[wave][(key[i] >> shift) & 255u], 1u);
+        for (int i = 0; i < kTkPer; ++i) key[i] = to_key(lds_tag, nxt[i]);
+        if (j0 + kRound < n) load_raw(lds_tag, j0 + kRound, kTkThreads, nxt);
+#pragma unroll
+        for (int i = 0; i < kTkPer; ++i) {
+          const int64_t j = j0 + (int64_t)i * kTkThreads;
+          if (j < n) {
+            if (pass == 0 && cached) s_key[j] = key[i];
+            if (((key[i] ^ prefix) & mask) == 0u) atomicAdd(&s_hist[wave][(key[i] >> shift) & 255u], 1u);
+          }
         }
       }
-    }
+    };
+    if (pass > 0 && cached) count(std::true_type{});
+    else count(std::false_type{});
     __syncthreads();
     // bin totals, then the bin where the count from the top reaches `remaining`
     if (tid < 256) {
@@ -191,41 +204,47 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
     }
     return before;
   };
-  auto load_chunk = [&](int64_t c0, uint32_t* key) { load_keys(cached, c0 + (int64_t)kTkPer * tid, 1, key); };
+  auto load_chunk = [&](auto lds_tag, int64_t c0, uint32_t* raw) { load_raw(lds_tag, c0 + (int64_t)kTkPer * tid, 1, raw); };
   uint32_t eq_base = 0, sel_base = 0;
-  uint32_t cur[kTkPer], nxt[kTkPer];
-  load_chunk(0, cur);
-  for (int64_t c0 = 0; c0 < n && sel_base < (uint32_t)k; c0 += kTkChunk) {
-    if (c0 + kTkChunk < n) load_chunk(c0 + kTkChunk, nxt);
-    const int64_t jt = c0 + (int64_t)kTkPer * tid;   // this thread's first column
-    uint32_t neq = 0;
+  auto compact = [&](auto lds_tag) {
+    uint32_t cur[kTkPer], nxt[kTkPer];
+    load_chunk(lds_tag, 0, cur);
+    for (int64_t c0 = 0; c0 < n && sel_base < (uint32_t)k; c0 += kTkChunk) {
 #pragma unroll
-    for (int i = 0; i < kTkPer; ++i) neq += (jt + i < n && cur[i] == K) ? 1u : 0u;
-    uint32_t eq_all, sel_all;
-    uint32_t e = eq_base + wg_scan(neq, 0, eq_all);
-    bool sel[kTkPer];
-    uint32_t nsel = 0;
+      for (int i = 0; i < kTkPer; ++i) cur[i] = to_key(lds_tag, cur[i]);
+      if (c0 + kTkChunk < n) load_chunk(lds_tag, c0 + kTkChunk, nxt);
+      const int64_t jt = c0 + (int64_t)kTkPer * tid;   // this thread's first column
+      uint32_t neq = 0;
 #pragma unroll
-    for (int i = 0; i < kTkPer; ++i) {
-      const bool in = jt + i < n;
-      const bool eq = in && cur[i] == K;
-      sel[i] = (in && cur[i] > K) || (eq && e < remaining);
-      e += eq ? 1u : 0u;
-      nsel += sel[i] ? 1u : 0u;
-    }
-    uint32_t pos = sel_base + wg_scan(nsel, 1, sel_all);
+      for (int i = 0; i < kTkPer; ++i) neq += (jt + i < n && cur[i] == K) ? 1u : 0u;
+      uint32_t eq_all, sel_all;
+      uint32_t e = eq_base + wg_scan(neq, 0, eq_all);
+      bool sel[kTkPer];
+      uint32_t nsel = 0;
 #pragma unroll
-    for (int i = 0; i < kTkPer; ++i) {
-      if (sel[i]) {
-        if (pos < (uint32_t)k) orow[pos] = (int32_t)(lo + jt + i);   // exactly k are selected
-        ++pos;
+      for (int i = 0; i < kTkPer; ++i) {
+        const bool in = jt + i < n;
+        const bool eq = in && cur[i] == K;
+        sel[i] = (in && cur[i] > K) || (eq && e < remaining);
+        e += eq ? 1u : 0u;
+        nsel += sel[i] ? 1u : 0u;
       }
-    }
-    eq_base += eq_all;
-    sel_base += sel_all;
+      uint32_t pos = sel_base + wg_scan(nsel, 1, sel_all);
 #pragma unroll
-    for (int i = 0; i < kTkPer; ++i) cur[i] = nxt[i];
-  }
+      for (int i = 0; i < kTkPer; ++i) {
+        if (sel[i]) {
+          if (pos < (uint32_t)k) orow[pos] = (int32_t)(lo + jt + i);   // exactly k are selected
+          ++pos;
+        }
+      }
+      eq_base += eq_all;
+      sel_base += sel_all;
+#pragma unroll
+      for (int i = 0; i < kTkPer; ++i) cur[i] = nxt[i];
+    }
+  };
+  if (cached) compact(std::true_type{});
+  else compact(std::false_type{});
 }
 
 }  // namespace dsa
