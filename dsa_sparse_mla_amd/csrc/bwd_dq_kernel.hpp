@@ -70,19 +70,29 @@ __device__ __forceinline__ void dq_issue_tile(const BwdArgs& a, const uint32_t* 
 // s dS row swizzle (8-byte units; rows of 64 bytes)
 __device__ __forceinline__ constexpr int dst_swz(int n) { return (n & 6) | ((n >> 3) & 1); }
 
+// HT head tiles of 16 per workgroup (2 or 4). With 2, S wave w takes key
+// block w & 1 of head tile w >> 1; with 4, S wave w takes both key blocks
+// of head tile w (each Q^T / dO^T operand then serves twice as many
+// products, and each tile is gathered once for 64 heads).
 // blockIdx.x = token * head_blocks + head block, over the tokens with
 // only[token] == 0 (only_nonzero = 0).
+template <int HT>
 __global__ void __launch_bounds__(64 * kDqWaves)
 sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
-  constexpr int HT = 2;
+  static_assert(HT == 2 || HT == 4, "32 or 64 heads per workgroup");
+  constexpr int KBW = HT / 2;   // key blocks per S wave
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[kDqStages * kBwStage];
-  // s dS, bf16 [32 heads][32 keys], one buffer per tile parity: logical
+  // s dS, bf16 [16 HT heads][32 keys], one buffer per tile parity: logical
   // 8-byte unit 2q of a head's row holds keys 4q .. 4q+3, unit 2q+1 keys
   // 16+4q .. 16+4q+3; unit u of head row h sits at u ^ dst_swz(h % 16), so
   // that the 16 lanes a b64 write serves together hit distinct banks
   __shared__ __attribute__((aligned(16))) uint8_t s_dst[2][16 * HT * 64];
   __shared__ __attribute__((aligned(16))) uint32_t s_rows[kSegment];   // compacted row ids
-  __shared__ int s_cnt[kChunks];
+  // the index stage's chunk counts share the s dS buffers (160 KB of LDS
+  // in all at 64 heads); a barrier ends each index segment, so no wave still
+  // reads s dS when the next segment's index stage writes them
+  int* const s_cnt = reinterpret_cast<int*>(&s_dst[1][0]);
+  static_assert(kChunks * 4 <= 16 * HT * 64, "the chunk counts fit a s dS buffer");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -106,13 +116,13 @@ sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
 
   // Barrier sequence per index segment, every wave: the index stage's two;
   // tile 0 landed; then after iteration j < ntiles: s dS of tile j written
-  // and tile j+1 landed. In iteration j the S waves form s dS of tile j and
+  // and tile j+1 landed; the dq waves' last products done. In iteration j the S waves form s dS of tile j and
   // the dq waves take the dq products of tile j - 1 and copy tile j + 2
   // into the stage of tile j - 2.
   if (is_s) {
     // ============================================================ S waves
-    // Key block kb, head tile ht; the lane's head is h0 + 16ht + n.
-    const int kb = sw & 1, ht = sw >> 1;
+    // Key blocks kb0 .. kb0 + KBW - 1, head tile ht; the lane's head is h0 + 16ht + n.
+    const int kb0 = HT == 2 ? (sw & 1) : 0, ht = HT == 2 ? (sw >> 1) : sw;
     const int head = h0 + 16 * ht + n;
     const bool head_ok = head < a.num_heads;
     // Q^T and dO^T as the MFMA B operand: lane holds columns 32c + 8g .. +7 of its head
@@ -135,15 +145,17 @@ sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
     // D from the prepass; LSE in log2 units, +inf for padded heads (P = 0 there)
     const float Dh = head_ok ? m.dbuf[token * m.d_st + head] : 0.f;
     const float l2 = head_ok ? a.lse[token * a.lse_st + head] * 1.4426950408889634f : INFINITY;
-    // A-operand offsets: key kb*16 + n, logical granule c' = 4c + g; latent
-    // c = 4i + c'' at a_lat[c''] + 256i, rope c = 16 + c'' at a_rope[c''].
-    uint32_t a_lat[4], a_rope[2];
-    {
-      const int r = kb * 16 + n;
+    // A-operand offsets of key block kb0 + b: key 16(kb0 + b) + n, logical
+    // granule c' = 4c + g; latent c = 4i + c'' at a_lat[b][c''] + 256i, rope
+    // c = 16 + c'' at a_rope[b][c''].
+    uint32_t a_lat[KBW][4], a_rope[KBW][2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) a_lat[c] = (uint32_t)(r * 1024 + 16 * ((4 * c + g) ^ bw_swz(r)));
+    for (int b = 0; b < KBW; ++b) {
+      const int r = (kb0 + b) * 16 + n;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) a_rope[c] = (uint32_t)(kBwLat + r * 128 + 16 * ((4 * c + g) ^ bw_swz_r(r)));
+      for (int c = 0; c < 4; ++c) a_lat[b][c] = (uint32_t)(r * 1024 + 16 * ((4 * c + g) ^ bw_swz(r)));
+#pragma unroll
+      for (int c = 0; c < 2; ++c) a_rope[b][c] = (uint32_t)(kBwLat + r * 128 + 16 * ((4 * c + g) ^ bw_swz_r(r)));
     }
 
     for (int seg = 0; seg < nseg; ++seg) {
@@ -153,42 +165,51 @@ sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
       __syncthreads();             // tile 0 landed
       for (int j = 0; j < ntiles; ++j) {
         const uint8_t* st = s_stage + (j % kDqStages) * kBwStage;
-        // ---- phase 1: S^T and dP^T of key block kb, head tile ht
-        float4_t acc_s = {0.f, 0.f, 0.f, 0.f}, acc_dp = {0.f, 0.f, 0.f, 0.f};
+        // ---- phase 1: S^T and dP^T of key blocks kb0 .., head tile ht
+        float4_t acc_s[KBW], acc_dp[KBW];
+#pragma unroll
+        for (int b = 0; b < KBW; ++b) acc_s[b] = acc_dp[b] = (float4_t){0.f, 0.f, 0.f, 0.f};
         {
-          auto a_read = [&](int c) {
-            return lds16(c < 16 ? st + a_lat[c & 3] + 256 * (c >> 2) : st + a_rope[c - 16]);
+          // read i: chunk i / KBW of key block kb0 + i % KBW
+          constexpr int kReads = KBW * (kDqk / 32);
+          auto a_read = [&](int i) {
+            const int c = i / KBW, b = i % KBW;
+            return lds16(c < 16 ? st + a_lat[b][c & 3] + 256 * (c >> 2) : st + a_rope[b][c - 16]);
           };
           // A operands read 6 ahead (pinned order: the scheduler would
           // otherwise sink each read next to its products)
           constexpr int kRing = 6;
           bf16x8_t ring[kRing];
 #pragma unroll
-          for (int c = 0; c < kRing; ++c) ring[c] = a_read(c);
+          for (int i = 0; i < kRing; ++i) ring[i] = a_read(i);
 #pragma unroll
-          for (int c = 0; c < kDqk / 32; ++c) {
-            const bf16x8_t av = ring[c % kRing];
-            if (c + kRing < kDqk / 32) ring[c % kRing] = a_read(c + kRing);
-            acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[c], acc_s, 0, 0, 0);
-            if (c < kDv / 32) acc_dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bdo[c], acc_dp, 0, 0, 0);
+          for (int i = 0; i < kReads; ++i) {
+            const int c = i / KBW, b = i % KBW;
+            const bf16x8_t av = ring[i % kRing];
+            if (i + kRing < kReads) ring[i % kRing] = a_read(i + kRing);
+            acc_s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[c], acc_s[b], 0, 0, 0);
+            if (c < kDv / 32) acc_dp[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bdo[c], acc_dp[b], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        // ---- phase 2: P and s*dS (lane: head 16ht + n, keys kb*16 + 4g + e)
-        {
-          const int lim = nvalid - j * kTileKeys;
+        // ---- phase 2: P and s*dS (lane: head 16ht + n, keys 16kb + 4g + e)
+        const int lim = nvalid - j * kTileKeys;
+#pragma unroll
+        for (int b = 0; b < KBW; ++b) {
+          const int kb = kb0 + b;
           float ds[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const bool ok = kb * 16 + 4 * g + e < lim;
-            const float p = ok ? __builtin_amdgcn_exp2f(acc_s[e] * a.scale_log2 - l2) : 0.f;
-            ds[e] = p * (acc_dp[e] - Dh) * a.scale;
+            const float p = ok ? __builtin_amdgcn_exp2f(acc_s[b][e] * a.scale_log2 - l2) : 0.f;
+            ds[e] = p * (acc_dp[b][e] - Dh) * a.scale;
           }
           *(uint2*)(s_dst[j & 1] + (16 * ht + n) * 64 + 8 * ((2 * g + kb) ^ dst_swz(n))) =
               (uint2){pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
         }
         __syncthreads();   // s dS of tile j written; tile j+1 landed
       }
+      __syncthreads();     // the dq waves' last products are done
     }
   } else {
     // ============================================================ dq waves
@@ -266,6 +287,7 @@ sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
         __syncthreads();   // s dS of tile j written; tile j+1 landed
       }
       phase3(ntiles - 1);
+      __syncthreads();   // s dS and the stages are free for the next segment
     }
 
     // ---------------------------------------------------------------- dq (fp32)

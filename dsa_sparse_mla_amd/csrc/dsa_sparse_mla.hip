@@ -604,7 +604,16 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
       hipLaunchKernelGGL(dsa::sparse_mla_bwd_kvw_kernel, kv_grid, dim3(256), 0, s, a, m);
       a.only = m.dup;
       a.only_nonzero = 0;
-      hipLaunchKernelGGL(dsa::sparse_mla_bwd_dq_kernel, dim3((unsigned)wgs), dim3(64 * dsa::kDqWaves), 0, s, a, m);
+      // dq: 64 heads per workgroup above 32 heads, else 32
+      if (num_heads > 32) {
+        dsa::BwdArgs a64 = a;
+        a64.head_blocks = (num_heads + 63) / 64;
+        hipLaunchKernelGGL(dsa::sparse_mla_bwd_dq_kernel<4>, dim3((unsigned)(num_tokens * a64.head_blocks)),
+                           dim3(64 * dsa::kDqWaves), 0, s, a64, m);
+      } else {
+        hipLaunchKernelGGL(dsa::sparse_mla_bwd_dq_kernel<2>, dim3((unsigned)wgs), dim3(64 * dsa::kDqWaves), 0, s,
+                           a, m);
+      }
       a.only_nonzero = 1;
       hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, s, a);
     } else {

@@ -378,6 +378,20 @@ def test_bwd_split_schedule(H):
     check_grad(dkv, rdkv, f"dkv split H={H}")
 
 
+@pytest.mark.parametrize("H", [32, 64])
+def test_bwd_split_long_rows(H):
+    """The split schedule on rows of 4500 entries, three 2048-entry index
+    segments per token in the dq pass (32 heads per workgroup at H = 32, 64
+    at H = 64), with -1 and out-of-range values making the segments ragged."""
+    T, N, topk = 40, 5000, 4500
+    assert split(H, N, topk, T)
+    q, kv, idx, dout = random_case(T, H, N, topk, seed=700 + H, dup=False)
+    dq, dkv = run(q, kv, idx, 1 / 24, dout)
+    rdq, rdkv = ref(q, kv, idx, 1 / 24, dout)
+    check_grad(np64(dq), rdq, f"dq split long rows H={H}")
+    check_grad(np64(dkv), rdkv, f"dkv split long rows H={H}")
+
+
 def test_bwd_split_causal_rows():
     """Causal rows at 64 heads (token t names min(t + 1, 256) of its keys 0..t,
     tail padding): blocks named by every later token, by a quarter of them,
