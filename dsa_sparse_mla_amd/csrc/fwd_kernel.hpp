@@ -49,6 +49,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dsa {
 
 constexpr int kDqk = 576;
@@ -161,13 +163,19 @@ __device__ __forceinline__ short4_t lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(
       (__attribute__((address_space(3))) uint8_t*)(p)));
 }
+// With one head tile (HT = 1) the waves split the keys as well as the value
+// columns: wave w scores key block w & 1 of each tile (16 keys) and takes
+// the PV product of those keys for value half w >> 1 (16x16x16 MFMAs), so
+// each score is computed twice instead of four times; the two waves of a
+// value half merge their partial outputs at the end.
 template <int HT>
 struct FwdShape {
   static constexpr int kHeads = 16 * HT;               // heads of the workgroup
-  static constexpr int kDvParts = kWaves / HT;         // waves sharing one head tile
+  static constexpr int kKeyBlocks = HT == 1 ? 1 : 2;   // 16-key blocks of a tile per wave
+  static constexpr int kDvParts = HT == 1 ? 2 : kWaves / HT;   // value slices of a head tile
   static constexpr int kDvCols = kDv / kDvParts;       // value columns of one wave
   static constexpr int kDvTiles = kDvCols / 16;        // 16-column MFMA tiles of one wave
-  static constexpr int kSSteps = 2 * (kDqk / 32);      // QK^T MFMAs per tile (2 blocks x 18 chunks)
+  static constexpr int kSSteps = kKeyBlocks * (kDqk / 32);   // QK^T MFMAs per tile (blocks x 18 chunks)
   static_assert(kWaves % HT == 0, "head tiles must divide the waves");
 };
 
@@ -360,8 +368,10 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
   const int nvalid = build_key_list<PAGED>(a, token, split, wave, lane, s_goff, s_cnt, [] {});
 
   // ---------------------------------------------------------------- per-wave state
+  constexpr int KBW = S::kKeyBlocks;
   const int ht = wave % HT;                  // head tile of this wave
-  const int dpart = wave / HT;               // value-column slice of this wave
+  const int dpart = HT == 1 ? wave >> 1 : wave / HT;   // value-column slice of this wave
+  const int kbw = HT == 1 ? wave & 1 : 0;    // first key block of this wave
   const int dv0 = dpart * S::kDvCols;
   const int head = hblock * S::kHeads + ht * 16 + hcol;
   const bool head_ok = head < a.num_heads;
@@ -433,11 +443,18 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
     const int off = c < 16 ? kbase[c & 3] + 64 * (c & ~3) + b * 16 * 1024 : rbase[c - 16] + b * 16 * 128;
     return *(const bf16x8_t*)(st + off);
   };
-  auto vread = [&](const uint8_t* st, int jt) {
+  // V^T operand of value tile jt: 8 keys (both blocks) for the 16x16x32
+  // MFMA, or with one key block per wave 4 keys of block kbw (16x16x16)
+  using VOp = std::conditional_t<KBW == 2, bf16x8_t, short4_t>;
+  auto vread = [&](const uint8_t* st, int jt) -> VOp {
     const uint8_t* p = st + vbase[jt & 7] + 256 * (jt >> 3);
-    const short4_t lo = lds_read_tr16(p);               // keys vr      (block 0): slots 0-3
-    const short4_t hi = lds_read_tr16(p + 16 * 1024);   // keys 16 + vr (block 1): slots 4-7
-    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    if constexpr (KBW == 2) {
+      const short4_t lo = lds_read_tr16(p);               // keys vr      (block 0): slots 0-3
+      const short4_t hi = lds_read_tr16(p + 16 * 1024);   // keys 16 + vr (block 1): slots 4-7
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return lds_read_tr16(p + kbw * 16 * 1024);          // keys 16 kbw + vr
+    }
   };
 
   // ---------------------------------------------------------------- 3-5. pipelined steps
@@ -451,32 +468,32 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
   // The softmax writes P^T of tile jn to pk_next; moving the reference max
   // only sets alpha, and the accumulator is rescaled after the step's last PV
   // MFMA (O of the previous tile must be complete first).
-  float4_t sacc[2];
-  bf16x8_t pk_cur = {}, pk_next = {};
-  float sp[2][4];
+  float4_t sacc[KBW];
+  VOp pk_cur = {}, pk_next = {};
+  float sp[KBW][4];
   float smx = -INFINITY;
   float alpha = 1.f;
 
   // Slice k of the softmax of tile jn. sacc[b][i] = raw score q . k of key
-  // 32jn + 16b + ksig + i for head `head`; the scale (>= 0, folded with
-  // log2 e) is applied inside the exponent.
+  // 32jn + 16(kbw + b) + ksig + i for head `head`; the scale (>= 0, folded
+  // with log2 e) is applied inside the exponent.
   auto soft_piece = [&](int k, int jn) {
     if (k == 0) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < KBW; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sp[b][i] = sacc[b][i];
       if ((jn + 1) * kTileKeys > nvalid) {   // the last tile: mask keys past the list
-        const int kb = jn * kTileKeys + ksig;
+        const int kb = jn * kTileKeys + 16 * kbw + ksig;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < KBW; ++b)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (kb + 16 * b + i >= nvalid) sp[b][i] = -INFINITY;
       }
       smx = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < KBW; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) smx = fmaxf(smx, sp[b][i]);
     } else if (k == 1) {
@@ -486,30 +503,38 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
       // Lazy rescaling: the reference max moves only when the tile max
       // exceeds it by more than kRescaleSlack (log2 units); until then
       // p = 2^(s - m_run) <= 2^kRescaleSlack. alpha = 1 unless it moves.
-      const float m_new = smx > m_run + kRescaleSlack ? fmaxf(m_run, smx) : m_run;   // finite: the tile holds a valid key
-      alpha = fast_exp2(m_run - m_new);
+      // (a tile always holds a valid key, but with one key block per wave
+      // the block may not: then smx = -inf and the reference stays)
+      const float m_new = smx > m_run + kRescaleSlack ? fmaxf(m_run, smx) : m_run;
+      alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
-    } else if (k == 3 || k == 4) {
+    } else if (k == 3 || (k == 4 && KBW == 2)) {
       const int b = k - 3;
 #pragma unroll
       for (int i = 0; i < 4; ++i) sp[b][i] = fast_exp2(__builtin_fmaf(sp[b][i], a.scale_log2, -m_run));
       if ((jn + 1) * kTileKeys > nvalid) {   // last tile: a masked slot has weight 0 (also when the scale is 0)
-        const int kb = jn * kTileKeys + ksig + 16 * b;
+        const int kb = jn * kTileKeys + ksig + 16 * (kbw + b);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (kb + i >= nvalid) sp[b][i] = 0.f;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) l_run += sp[b][i];
-    } else {
-      // P^T as the B operand of the tile's 32-key step: slots 0-3 = block 0, 4-7 = block 1
-      uint4 w;
-      w.x = pack_bf16x2(sp[0][0], sp[0][1]);
-      w.y = pack_bf16x2(sp[0][2], sp[0][3]);
-      w.z = pack_bf16x2(sp[1][0], sp[1][1]);
-      w.w = pack_bf16x2(sp[1][2], sp[1][3]);
-      pk_next = __builtin_bit_cast(bf16x8_t, w);
+    } else if (k == 5) {
+      // P^T as the B operand of the tile's PV step: slots 0-3 = block 0, 4-7
+      // = block 1 (32-key step), or the wave's block alone (16-key step)
+      if constexpr (KBW == 2) {
+        uint4 w;
+        w.x = pack_bf16x2(sp[0][0], sp[0][1]);
+        w.y = pack_bf16x2(sp[0][2], sp[0][3]);
+        w.z = pack_bf16x2(sp[1][0], sp[1][1]);
+        w.w = pack_bf16x2(sp[1][2], sp[1][3]);
+        pk_next = __builtin_bit_cast(bf16x8_t, w);
+      } else {
+        const uint2 w = {pack_bf16x2(sp[0][0], sp[0][1]), pack_bf16x2(sp[0][2], sp[0][3])};
+        pk_next = __builtin_bit_cast(short4_t, w);
+      }
       // anchor the softmax here, beside the PV MFMAs (no sinking past the rescale)
       asm volatile("" : "+v"(pk_next), "+v"(l_run));
     }
@@ -531,30 +556,35 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
   };
   auto step = [&](const uint8_t* st_s, bool do_s, int jn, const uint8_t* st_pv, bool do_pv, int issue_j,
                   Fp8Share& f8) {
-    constexpr int kS = S::kSSteps;        // 36 QK^T MFMAs: (chunk t/2, block t%2)
+    constexpr int kS = S::kSSteps;        // QK^T MFMAs: (chunk t / KBW, block kbw + t % KBW)
     constexpr int kP = S::kDvTiles;       // PV MFMAs: value tile u
     constexpr int kPA = kP / 2;           // PV MFMAs placed in phase A
     constexpr int kKA = 4, kVA = 3;       // read-ahead (<= 15 LDS operations in flight)
     constexpr int kPieces = 6;
-    bf16x8_t kr[kKA + 1], vrg[kVA + 1];
+    bf16x8_t kr[kKA + 1];
+    VOp vrg[kVA + 1];
     if (do_pv) {
 #pragma unroll
       for (int u = 0; u < kVA; ++u) vrg[u] = vread(st_pv, u);
     }
     auto pv_mfma = [&](int u) {
       if (u + kVA < kP) vrg[(u + kVA) % (kVA + 1)] = vread(st_pv, u + kVA);
-      oacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vrg[u % (kVA + 1)], pk_cur, oacc[u], 0, 0, 0);
+      if constexpr (KBW == 2)
+        oacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vrg[u % (kVA + 1)], pk_cur, oacc[u], 0, 0, 0);
+      else
+        oacc[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vrg[u % (kVA + 1)], pk_cur, oacc[u], 0, 0, 0);
     };
     if (do_s) {
-      sacc[0] = sacc[1] = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < kKA; ++t) kr[t] = kread(st_s, t >> 1, t & 1);
+      for (int b = 0; b < KBW; ++b) sacc[b] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < kKA; ++t) kr[t] = kread(st_s, t / KBW, kbw + t % KBW);
       // phase A
 #pragma unroll
       for (int t = 0; t < kS; ++t) {
-        if (t + kKA < kS) kr[(t + kKA) % (kKA + 1)] = kread(st_s, (t + kKA) >> 1, (t + kKA) & 1);
-        sacc[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[t % (kKA + 1)], qreg[t >> 1], sacc[t & 1], 0, 0, 0);
-        if (t >= kS - 2) asm volatile("" : "+v"(sacc[t & 1]));   // scores in VGPRs: read by the softmax
+        if (t + kKA < kS) kr[(t + kKA) % (kKA + 1)] = kread(st_s, (t + kKA) / KBW, kbw + (t + kKA) % KBW);
+        sacc[t % KBW] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[t % (kKA + 1)], qreg[t / KBW], sacc[t % KBW], 0, 0, 0);
+        if (t >= kS - KBW) asm volatile("" : "+v"(sacc[t % KBW]));   // scores in VGPRs: read by the softmax
         if (do_pv && (t & 1) && (t >> 1) < kPA) pv_mfma(t >> 1);
         if (t == 3 && issue_j >= 0) gather(issue_j, f8);
         __builtin_amdgcn_sched_barrier(0);
@@ -650,6 +680,30 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
   // ---------------------------------------------------------------- 6. epilogue
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
+  float m_fin = m_run;
+  if constexpr (KBW == 1) {
+    // The two waves of a value half merge: the wave of key block 1 hands its
+    // unnormalised O, reference max and row sum to the wave of key block 0
+    // through the stage memory, idle once every wave has left the loop.
+    __syncthreads();
+    float* xo = reinterpret_cast<float*>(s_stage) + dpart * (S::kDvTiles * 256 + 128);
+    if (kbw == 1) {
+#pragma unroll
+      for (int jt = 0; jt < S::kDvTiles; ++jt) *(float4_t*)(xo + 4 * (jt * 64 + lane)) = oacc[jt];
+      xo[S::kDvTiles * 256 + lane] = m_run;
+      xo[S::kDvTiles * 256 + 64 + lane] = l_tot;
+    }
+    __syncthreads();
+    if (kbw == 1) return;   // uniform per wave; no barrier follows
+    const float m1 = xo[S::kDvTiles * 256 + lane], l1 = xo[S::kDvTiles * 256 + 64 + lane];
+    const float M = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);   // a block with no key has weight 0
+    const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
+#pragma unroll
+    for (int jt = 0; jt < S::kDvTiles; ++jt) oacc[jt] = oacc[jt] * a0 + *(const float4_t*)(xo + 4 * (jt * 64 + lane)) * a1;
+    l_tot = l_tot * a0 + l1 * a1;
+    m_fin = M;
+  }
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
 
   if (head_ok) {
@@ -664,14 +718,14 @@ sparse_mla_fwd_kernel(const FwdArgs a) {
         *(uint2*)(op + 16 * jt) = w;
       }
       if (dpart == 0 && kq == 0)
-        a.lse[token * a.lse_st + head] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        a.lse[token * a.lse_st + head] = l_tot > 0.f ? (m_fin + __log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
       const int64_t prow = (token * a.splits + split) * a.num_heads + head;
       float* pp = a.part_o + prow * kDv + dv0 + kq * 4;
 #pragma unroll
       for (int jt = 0; jt < S::kDvTiles; ++jt) *(float4_t*)(pp + 16 * jt) = oacc[jt] * inv_l;
       if (dpart == 0 && kq == 0) {
-        a.part_ml[prow * 2] = m_run;
+        a.part_ml[prow * 2] = m_fin;
         a.part_ml[prow * 2 + 1] = l_tot;
       }
     }
