@@ -3,28 +3,31 @@
 // Above 16 heads the token-major kernel's dkv atomics (576 floats per token,
 // key and 32-head block) bound the backward. The split schedule computes the
 // two gradients in separate passes, each written by its owner: dq by the
-// token-major kernel with its dkv phase compiled out (one workgroup owns a
-// token's heads), and dkv by this kv-major pass (one workgroup owns 64 kv
-// rows). Each pass recomputes P from the forward's LSE.
+// dq pass (bwd_dq_kernel.hpp: one workgroup owns a token's heads), and dkv
+// by this kv-major pass (one workgroup owns 64 kv rows). Each pass
+// recomputes P from the forward's LSE.
 //
 // One workgroup = 4 waves = (64 kv rows r0 .., chunk of 256 tokens). It
 // collects the chunk's tokens whose occupancy masks name any of its rows and
 // takes them in steps of one token and 32 heads (a head group; 64 heads take
-// two steps per token). Wave w owns rows r0 + 16w .. +15 for the whole chunk:
-//   * their K rows (all 576 columns) stay in registers as MFMA B operands;
-//   * S^T = q K^T (16x16x32 MFMA, heads as M, the wave's rows as N) and
-//     dP^T = dO V^T, with q and dO of the step read from LDS as A operands;
+// two steps per token). The waves pair up: wave (rh, ch) owns rows
+// r0 + 32rh .. +31 for the whole chunk and head tile ch of each step:
+//   * its K rows (all 576 columns) stay in registers as MFMA B operands;
+//   * S^T = q K^T (16x16x32 MFMA, heads as M, the rows as N) and
+//     dP^T = dO V^T of head tile ch, with q and dO of the step read from LDS
+//     as A operands, each read feeding the two row tiles;
 //   * P and s*dS in the accumulator layout: lane (g, n) holds row n and
-//     heads 4g .. 4g+3, 16+4g .. 16+4g+3. That is exactly the A operand of a
-//     16x16x32 MFMA over the 32 heads with its k-slots permuted the same way,
-//     so P and dS never go through LDS;
-//   * dkv[16 rows x 576] += (s dS) q + P dO (the latter on the first 512
-//     columns), with q^T and dO^T read transposed from LDS
+//     heads 4g .. 4g+3 of its head tile. The pair swaps them through LDS, so
+//     that each wave holds heads 4g .. 4g+3 and 16+4g .. 16+4g+3: the A
+//     operand of a 16x16x32 MFMA over the 32 heads with its k-slots permuted
+//     the same way;
+//   * dkv[32 rows x half ch of the columns] += (s dS) q + P dO (the latter on
+//     the first 512 columns), with q^T and dO^T read transposed from LDS
 //     (ds_read_b64_tr_b16, rows 4g.. and 16+4g.. give the permuted k-slots).
 // dkv stays in registers over the chunk and is added once per workgroup.
 // Each step's q, dO, LSE and D are copied HBM -> LDS by the 4 waves
-// (global_load_lds) during the previous step: one barrier per step, no
-// other synchronisation.
+// (global_load_lds) during the previous step. Two barriers per step: the
+// copies landed, and the P/dS swap.
 //
 // Masked rows (not named by the step's token) and padded heads (beyond
 // num_heads: they alias the last head, with LSE = +inf) get P = 0 and dS = 0.
