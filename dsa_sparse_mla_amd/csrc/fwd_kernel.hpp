@@ -24,11 +24,15 @@
 // stream interleaves their MFMAs and LDS reads, and each hides the other's
 // latency.
 //
-// Work split: the workgroup's heads form HT tiles of 16. Wave w computes S
-// for head tile w % HT over every key of the tile, and PV for that head tile
-// over its own slice of 512 * HT / 4 value columns. With HT < 4 the waves of
-// one head tile repeat the (small) S product instead of exchanging P, so no
-// wave ever waits for another inside the key loop except at the tile barrier.
+// Work split: the workgroup's heads form HT tiles of 16. With HT = 2, wave w
+// computes S for head tile w % 2 over every key of the tile, and PV for that
+// head tile over its own half of the 512 value columns: the two waves of a
+// head tile repeat the S product instead of exchanging P. With HT = 1, wave
+// w scores key block w & 1 of each tile (16 keys) and takes the PV product
+// of those keys for value half w >> 1 on 16x16x16 MFMAs; the two waves of a
+// value half keep separate softmax state and merge their partial outputs
+// once, at the end. Either way no wave waits for another inside the key
+// loop except at the tile barrier.
 //
 // LDS stage layout (32 keys, 36 KB): a latent region of 32 rows x 1 KB
 // (dims 0..511, i.e. V) and a rope region of 32 rows x 128 B (dims 512..575).
