@@ -440,6 +440,39 @@ def test_bwd_split_strided():
     check_grad(np64(dkv), rdkv, "dkv strided split")
 
 
+def test_bwd_varlen16k_full_sampled():
+    """The packed-document prefill at full size (16384 tokens in documents,
+    64 heads, topk 2048, the split schedule), sampled as the wide case: dq
+    of tokens at document edges and mid-document, and dkv of two rows 60
+    before the end of every document (each named only by later tokens of
+    its own document, about 50 of them), with every token that names them
+    given to the oracle."""
+    dsa = _dsa()
+    d = workloads.make_flat("varlen16k", device=DEV)
+    T, H = d["q"].shape[:2]
+    N = d["kv"].shape[0]
+    assert split(H, N, 2048, T)
+    cu = d["cu_seqlens"].numpy()
+    dout = workloads.randn_bf16((T, H, 512), 78, DEV)
+    idx = d["indices"].cpu().numpy()
+    rows = np.concatenate([np.arange(int(e) - 60, int(e) - 58) for e in cu[1:]])
+    toks = np.array([0, int(cu[1]), int(cu[1]) - 1, int(cu[len(cu) // 2]) + 5, T - 1])
+    naming = np.flatnonzero(np.isin(idx, rows).any(axis=1))
+    U = np.union1d(naming, toks)
+    assert len(U) < 400
+    q_u, kv_c = np64(d["q"][torch.from_numpy(U).to(DEV)]), np64(d["kv"])
+    o_u, l_u = sparse_mla_fwd_ref(q_u, kv_c, idx[U], d["sm_scale"])
+    out, lse = dsa.sparse_mla_fwd(d["q"], d["kv"], d["indices"], d["sm_scale"])
+    ut = torch.from_numpy(U).to(DEV)
+    out[ut] = torch.from_numpy(o_u).to(torch.bfloat16).to(DEV)
+    lse[ut] = torch.from_numpy(l_u).float().to(DEV)
+    dq, dkv = dsa.sparse_mla_bwd(d["q"], d["kv"], d["indices"], d["sm_scale"], out, lse, dout)
+    torch.cuda.synchronize()
+    rdq, rdkv = sparse_mla_bwd_ref(q_u, kv_c, idx[U], d["sm_scale"], np64(dout[ut]))
+    check_grad(np64(dq[ut]), rdq, "dq varlen16k sampled tokens")
+    check_grad(np64(dkv[torch.from_numpy(rows).to(DEV)]), rdkv[rows], "dkv varlen16k sampled rows")
+
+
 def test_bwd_wide_full_sampled():
     """The wide-head prefill at full size (8192 tokens, 64 heads, topk 2048,
     the split schedule), in the configuration bench.py --op bwd times, on
