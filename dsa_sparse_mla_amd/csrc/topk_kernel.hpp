@@ -116,12 +116,15 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
   };
 
   // ---------------------------------------------------------------- 1. radix select
+  // Two barriers per pass: counts complete, then the chosen digit published.
+  // Each wave counts into its own histogram row and clears it itself after
+  // the second barrier (wave 0 reads every row before that barrier).
   uint32_t prefix = 0, mask = 0;
   uint32_t remaining = (uint32_t)k;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_hist[wave][4 * lane + i] = 0u;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < kTkWaves * 256; i += kTkThreads) (&s_hist[0][0])[i] = 0u;
-    __syncthreads();
     // kTkPer keys per thread and round; the next round's entries are
     // loaded before this round's are counted (one loop per source)
     auto count = [&](auto lds_tag) {
@@ -145,37 +148,39 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
     };
     if (pass > 0 && cached) count(std::true_type{});
     else count(std::false_type{});
-    __syncthreads();
-    // bin totals, then the bin where the count from the top reaches `remaining`
-    if (tid < 256) {
-      uint32_t c = 0;
+    __syncthreads();   // every wave's counts are in
+    if (wave == 0) {
+      // lane l takes bins 4l .. 4l+3: their totals over the waves, the keys
+      // in higher bins (a suffix sum over the lanes), then the bin where the
+      // count from the top reaches `remaining`
+      uint32_t c[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int w = 0; w < kTkWaves; ++w) c += s_hist[w][tid];
-      uint32_t incl = c;   // suffix sum over the wave's 64 bins (bins tid .. 64 wave + 63)
+      for (int w = 0; w < kTkWaves; ++w)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] += s_hist[w][4 * lane + i];
+      const uint32_t tot = (c[0] + c[1]) + (c[2] + c[3]);
+      uint32_t incl = tot;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const uint32_t o = __shfl_down(incl, off, 64);
         if (lane + off < 64) incl += o;
       }
-      if (lane == 0) s_wsum[0][wave] = incl;
-      s_hist[0][tid] = c;         // wave 0's copy is no longer needed: keep the totals
-      s_hist[1][tid] = incl - c;  // and the count above each bin inside its wave
-    }
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t above = s_hist[1][tid];
-      for (int w = wave + 1; w < 4; ++w) above += s_wsum[0][w];
-      const uint32_t c = s_hist[0][tid];
-      if (above < remaining && remaining <= above + c) {
-        s_state[0] = (uint32_t)tid;
-        s_state[1] = remaining - above;
+      uint32_t above = incl - tot;   // keys in bins 4l + 4 ..
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (above < remaining && remaining <= above + c[i]) {
+          s_state[0] = (uint32_t)(4 * lane + i);
+          s_state[1] = remaining - above;
+        }
+        above += c[i];
       }
     }
-    __syncthreads();
+    __syncthreads();   // the digit is published; wave 0 is done reading the counts
     prefix |= s_state[0] << shift;
     mask |= 255u << shift;
     remaining = s_state[1];
-    __syncthreads();   // s_state and s_hist are rewritten by the next pass
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_hist[wave][4 * lane + i] = 0u;   // this wave's row, for the next pass
   }
   const uint32_t K = prefix;    // the k-th key; `remaining` keys equal to it are taken
 
