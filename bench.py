@@ -53,7 +53,7 @@ BWD_BYTES_PER_KEY = ROW_BYTES
 # kernel sources behind each op's measurements (the launch code is in the .hip)
 OP_SOURCES = {
     "fwd": ("dsa_sparse_mla.hip", "fwd_kernel.hpp", "fwd_kernel_ws.hpp"),
-    "bwd": ("dsa_sparse_mla.hip", "fwd_kernel.hpp", "bwd_kernel.hpp", "bwd_kvw_kernel.hpp", "bwd_dq_kernel.hpp"),
+    "bwd": ("dsa_sparse_mla.hip", "fwd_kernel.hpp", "bwd_kernel.hpp", "bwd_dq_kernel.hpp", "bwd_dkv_kernel.hpp"),
     "topk": ("dsa_sparse_mla.hip", "topk_kernel.hpp"),
 }
 
@@ -93,7 +93,7 @@ COPY_BYTES = 256 << 20   # the calibration copy reads and writes this many bytes
 FWD_KERNEL = re.compile(r"sparse_mla_fwd(_ws)?_kernel")   # the forward kernels' names
 # the kernels of one backward call: the dkv fill (once per call), the kv-major
 # prepass and pass, and the token-major kernel
-BWD_KERNEL = re.compile(r"dkv_zero_kernel|sparse_mla_bwd_(prep_|kv_|kvw_|dq_)?kernel")
+BWD_KERNEL = re.compile(r"dkv_zero_kernel|sparse_mla_bwd_(prep_|kv_|dkv_|dq_)?kernel")
 BWD_CALL_MARK = re.compile(r"dkv_zero_kernel")
 TOPK_KERNEL = re.compile(r"topk_select_kernel")
 OP_KERNEL = {"fwd": FWD_KERNEL, "bwd": BWD_KERNEL, "topk": TOPK_KERNEL}

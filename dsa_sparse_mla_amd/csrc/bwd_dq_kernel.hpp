@@ -70,6 +70,24 @@ __device__ __forceinline__ void dq_issue_tile(const BwdArgs& a, const uint32_t* 
 // s dS row swizzle (8-byte units; rows of 64 bytes)
 __device__ __forceinline__ constexpr int dst_swz(int n) { return (n & 6) | ((n >> 3) & 1); }
 
+// 4 x 4 transpose of bf16 values over the lanes of a quad (i = lane & 3).
+// On entry lane i holds row i: x0 = (v0, v1), x1 = (v2, v3); on exit it holds
+// element i of rows 0 .. 3, packed the same way. Two quad permutes (DPP).
+__device__ __forceinline__ uint2 quad_transpose_bf16(uint32_t x0, uint32_t x1, int i) {
+  const bool b1 = (i & 2) != 0, b0 = (i & 1) != 0;
+  // exchange with lane i ^ 2: lanes 0, 1 keep elements 0, 1; lanes 2, 3 elements 2, 3
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(b1 ? x0 : x1), 0x4E, 0xF, 0xF, false);
+  const uint32_t A = b1 ? r1 : x0;   // row i & 1
+  const uint32_t B = b1 ? x1 : r1;   // row (i & 1) + 2
+  // exchange with lane i ^ 1: an even lane keeps the low elements, an odd lane the high ones
+  const uint32_t send = b0 ? ((A & 0xFFFFu) | (B << 16)) : ((A >> 16) | (B & 0xFFFF0000u));
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+  uint2 o;
+  o.x = b0 ? ((r2 & 0xFFFFu) | (A & 0xFFFF0000u)) : ((A & 0xFFFFu) | (r2 << 16));
+  o.y = b0 ? ((r2 >> 16) | (B & 0xFFFF0000u)) : ((B & 0xFFFFu) | (r2 & 0xFFFF0000u));
+  return o;
+}
+
 // HT head tiles of 16 per workgroup (2 or 4). With 2, S wave w takes key
 // block w & 1 of head tile w >> 1; with 4, S wave w takes both key blocks
 // of head tile w (each Q^T / dO^T operand then serves twice as many
@@ -145,6 +163,16 @@ sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
     // D from the prepass; LSE in log2 units, +inf for padded heads (P = 0 there)
     const float Dh = head_ok ? m.dbuf[token * m.d_st + head] : 0.f;
     const float l2 = head_ok ? a.lse[token * a.lse_st + head] * 1.4426950408889634f : INFINITY;
+    // P and s dS for the dkv pass: after the quad transpose, lane (g, n)
+    // holds key 16kb + 4g + (n & 3) and heads 16ht + 4(n >> 2) .. +3; they go
+    // to the key's rank in the head group's run, heads in order (the four
+    // lanes of a key write the head tile's 32 contiguous bytes)
+    const int hg = (h0 + 16 * ht) >> 5;
+    const bool pds_ok = hg < m.groups;
+    uint8_t* const pds_tok = reinterpret_cast<uint8_t*>(m.pds) + ((token * m.groups + hg) * m.cap) * 128 +
+                             32 * (ht & 1) + 8 * (n >> 2);
+    const int32_t* const rank_tok = m.rank + token * m.cap;
+    int cbase = 0;   // valid entries of the earlier index segments
     // A-operand offsets of key block kb0 + b: key 16(kb0 + b) + n, logical
     // granule c' = 4c + g; latent c = 4i + c'' at a_lat[b][c''] + 256i, rope
     // c = 16 + c'' at a_rope[b][c''].
@@ -162,9 +190,37 @@ sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
       const int nvalid = build_key_list<false, kDqWaves>(fa, token, seg, wave, lane, s_rows, s_cnt, [] {});
       const int ntiles = (nvalid + kTileKeys - 1) / kTileKeys;
       if (ntiles == 0) continue;   // uniform
+      // ranks of the keys this lane stores in phase 2 of tile j, read one
+      // tile ahead and before the stores of the tile in between (the wait
+      // for a read would otherwise also wait for those stores)
+      auto read_ranks = [&](int j, int (&rk)[KBW]) {
+#pragma unroll
+        for (int b = 0; b < KBW; ++b) {
+          const int kk = j * kTileKeys + 16 * (kb0 + b) + 4 * g + (n & 3);
+          rk[b] = rank_tok[cbase + (kk < nvalid ? kk : 0)];
+        }
+      };
+      int rk[KBW], rk_next[KBW];
+      read_ranks(0, rk);
+      // P and s dS of the previous tile, stored during this tile's products
+      // (issued at the end of phase 2 they waited, before the barrier, behind
+      // the dq waves' copies in the CU's memory queue)
+      uint2 pend_p[KBW], pend_d[KBW];
+      int pend_rk[KBW];
+      bool pend_ok[KBW];
+#pragma unroll
+      for (int b = 0; b < KBW; ++b) pend_ok[b] = false;
+      auto store_pending = [&](int b) {
+        if (pend_ok[b]) {
+          uint8_t* const d = pds_tok + (int64_t)pend_rk[b] * 128;
+          *(uint2*)d = pend_p[b];
+          *(uint2*)(d + 64) = pend_d[b];
+        }
+      };
       __syncthreads();             // tile 0 landed
       for (int j = 0; j < ntiles; ++j) {
         const uint8_t* st = s_stage + (j % kDqStages) * kBwStage;
+        const int lim = nvalid - j * kTileKeys;
         // ---- phase 1: S^T and dP^T of key blocks kb0 .., head tile ht
         float4_t acc_s[KBW], acc_dp[KBW];
 #pragma unroll
@@ -190,26 +246,37 @@ sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
             acc_s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[c], acc_s[b], 0, 0, 0);
             if (c < kDv / 32) acc_dp[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bdo[c], acc_dp[b], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
+            if (i % 8 == 3 && i / 8 < KBW) store_pending(i / 8);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
         // ---- phase 2: P and s*dS (lane: head 16ht + n, keys 16kb + 4g + e)
-        const int lim = nvalid - j * kTileKeys;
 #pragma unroll
         for (int b = 0; b < KBW; ++b) {
           const int kb = kb0 + b;
-          float ds[4];
+          float pv[4], ds[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const bool ok = kb * 16 + 4 * g + e < lim;
-            const float p = ok ? __builtin_amdgcn_exp2f(acc_s[b][e] * a.scale_log2 - l2) : 0.f;
-            ds[e] = p * (acc_dp[b][e] - Dh) * a.scale;
+            pv[e] = ok ? __builtin_amdgcn_exp2f(acc_s[b][e] * a.scale_log2 - l2) : 0.f;
+            ds[e] = pv[e] * (acc_dp[b][e] - Dh) * a.scale;
           }
-          *(uint2*)(s_dst[j & 1] + (16 * ht + n) * 64 + 8 * ((2 * g + kb) ^ dst_swz(n))) =
-              (uint2){pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
+          const uint32_t d01 = pack_bf16x2(ds[0], ds[1]), d23 = pack_bf16x2(ds[2], ds[3]);
+          *(uint2*)(s_dst[j & 1] + (16 * ht + n) * 64 + 8 * ((2 * g + kb) ^ dst_swz(n))) = (uint2){d01, d23};
+          if (b == 0) read_ranks(j + 1 < ntiles ? j + 1 : j, rk_next);
+          pend_p[b] = quad_transpose_bf16(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), n & 3);
+          pend_d[b] = quad_transpose_bf16(d01, d23, n & 3);
+          pend_rk[b] = rk[b];
+          pend_ok[b] = pds_ok && kb * 16 + 4 * g + (n & 3) < lim;
         }
+#pragma unroll
+        for (int b = 0; b < KBW; ++b) rk[b] = rk_next[b];
         __syncthreads();   // s dS of tile j written; tile j+1 landed
       }
+#pragma unroll
+      for (int b = 0; b < KBW; ++b) store_pending(b);   // the last tile's
       __syncthreads();     // the dq waves' last products are done
+      cbase += nvalid;
     }
   } else {
     // ============================================================ dq waves

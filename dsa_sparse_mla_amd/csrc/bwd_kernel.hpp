@@ -413,6 +413,9 @@ sparse_mla_bwd_kernel(const BwdArgs a) {
 // row r named), D = dO . O per head, and zeroes the token's dq. A token whose
 // row names some kv row twice is left to the token-major kernel (its masks
 // stay 0 and only[t] = 1), so duplicates keep counting once per occurrence.
+// For the split schedule it also numbers the token's named rows in row order
+// (their rank): the rank of each valid entry, and per 256-row block the
+// number of named rows below it.
 
 constexpr int kKvChunk = 64;        // tokens per kv-major workgroup (one wave's ballot)
 constexpr int kKvMaxWords = 8192;   // mask words per token row held in LDS (kv rows <= 262144)
@@ -424,12 +427,25 @@ struct KvMajorArgs {
   int64_t d_st;       // heads per token row of dbuf: 16, or num_heads above 16
   int32_t num_words;  // ceil(num_kv / 32)
   int32_t zero_dq;    // 1: the prepass zeroes dq (the kv-major pass adds into it)
+  // Split schedule only (null otherwise). A token's named rows, ordered by
+  // row id, are numbered 0, 1, ... (their rank); the dq pass stores P and
+  // s*dS of each named row at its rank, so that the dkv pass finds the named
+  // rows of any 256-row block as one contiguous run.
+  int32_t* pre;       // i32 [num_blk][num_tokens]: named rows of token t below row 256b
+  int32_t* rank;      // i32 [num_tokens][cap]: rank of the token's c-th valid entry (index-row order)
+  uint16_t* pds;      // bf16 [num_tokens][groups][cap][64]: per rank, P of the group's 32 heads, then s*dS
+  int64_t cap;        // entries per token in rank and pds (topk)
+  int32_t groups;     // head groups of 32: ceil(num_heads / 32)
+  int32_t num_blk;    // ceil(num_words / 8): blocks of 256 rows
+  uint32_t* queue;    // u32 [8]: the dkv pass's work-queue counters (the prepass clears them)
 };
 
 __global__ void __launch_bounds__(256)
 sparse_mla_bwd_prep_kernel(const BwdArgs a, const KvMajorArgs m) {
   __shared__ uint32_t s_bm[kKvMaxWords];
+  __shared__ int s_wp[kKvMaxWords];   // split schedule: named rows below each word
   __shared__ uint32_t s_dup;
+  __shared__ int s_sum[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t token = blockIdx.x;
   for (int w = tid; w < m.num_words; w += 256) s_bm[w] = 0u;
@@ -463,6 +479,51 @@ sparse_mla_bwd_prep_kernel(const BwdArgs a, const KvMajorArgs m) {
   const uint32_t dup = s_dup;
   if (tid == 0) m.dup[token] = dup;
   for (int w = tid; w < m.num_words; w += 256) m.mask[(int64_t)w * a.num_tokens + token] = dup ? 0u : s_bm[w];
+  if (m.queue != nullptr && token == 0 && tid < 8) m.queue[tid] = 0u;
+  if (m.rank == nullptr || dup) return;   // uniform
+
+  // ---- split schedule: ranks. s_wp[w] = named rows below row 32w (an
+  // exclusive scan of the words' popcounts; thread i takes a run of words).
+  const int per = (m.num_words + 255) / 256;
+  const int w0 = min(tid * per, m.num_words), w1 = min(w0 + per, m.num_words);
+  int run = 0;
+  for (int w = w0; w < w1; ++w) run += __popc(s_bm[w]);
+  int incl = run;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_sum[wave] = incl;
+  __syncthreads();
+  int base = incl - run;
+  for (int i = 0; i < wave; ++i) base += s_sum[i];
+  for (int w = w0; w < w1; ++w) {
+    s_wp[w] = base;
+    base += __popc(s_bm[w]);
+  }
+  __syncthreads();
+  for (int b = tid; b < m.num_blk; b += 256) m.pre[(int64_t)b * a.num_tokens + token] = s_wp[8 * b];
+  // the c-th valid entry of the row (the order of the dq pass's key list)
+  int cbase = 0;
+  int32_t* const rk = m.rank + token * m.cap;
+  for (int j0 = 0; j0 < a.topk; j0 += 256) {
+    const int j = j0 + tid;
+    const int32_t v = j < a.topk ? row[j] : -1;
+    const bool ok = v >= 0 && (int64_t)v < a.num_kv;
+    const uint64_t bal = __ballot(ok);
+    __syncthreads();   // the previous round's reads of s_sum are done
+    if (lane == 0) s_sum[wave] = __popcll(bal);
+    __syncthreads();
+    int before = cbase;
+    for (int i = 0; i < wave; ++i) before += s_sum[i];
+    if (ok) {
+      const int c = before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      rk[c] = s_wp[v >> 5] + __popc(s_bm[v >> 5] & ((1u << (v & 31)) - 1u));
+    }
+    cbase += s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
+  }
 }
 
 // One workgroup = (two kv blocks bp = rows 64bp .. 64bp+63, token chunk c);

@@ -16,8 +16,8 @@
 #include "fwd_kernel.hpp"
 #include "fwd_kernel_ws.hpp"
 #include "bwd_kernel.hpp"
-#include "bwd_kvw_kernel.hpp"
 #include "bwd_dq_kernel.hpp"
+#include "bwd_dkv_kernel.hpp"
 #include "topk_kernel.hpp"
 
 namespace {
@@ -182,11 +182,14 @@ void* scratch_address(int dev) {
 // at 16, 4.7x on packed documents at 8 heads. Its workspace holds the
 // per-token occupancy masks ([word][token] u32), the per-token repeat flags
 // and D = dout . out per (token, head); above 1 GiB of it the token-major
-// kernel runs instead.
+// kernel runs instead. The split schedule's workspace adds the prepass's
+// ranks (per 256-row block and per index entry) and the dq pass's P and
+// s*dS, 128 bytes per (token, entry, 32-head group): topk x H x 4 bytes per
+// token. Above 64 GiB of it the token-major kernel runs instead.
 struct BwdPlan {
   int schedule = DSA_BWD_TOKEN_MAJOR;
-  int64_t words = 0, chunks = 0;
-  int64_t dup_off = 0, d_off = 0;
+  int64_t words = 0, chunks = 0, blk = 0, groups = 0;
+  int64_t dup_off = 0, d_off = 0, pre_off = 0, rank_off = 0, pds_off = 0;
   int64_t ws_bytes = 0;
 };
 
@@ -195,22 +198,37 @@ void bwd_plan(int64_t T, int32_t H, int64_t N, int32_t topk, BwdPlan* p) {
   if (T <= 0 || N <= 0) return;
   const int64_t words = (N + 31) / 32;
   const bool wide = H > 16;
-  const int64_t chunks = (T + (wide ? dsa::kKwChunk : dsa::kKvChunk) - 1) / (wide ? dsa::kKwChunk : dsa::kKvChunk);
+  const int64_t chunk = wide ? dsa::kDkChunk : dsa::kKvChunk;
+  const int64_t chunks = (T + chunk - 1) / chunk;
+  const int64_t blk = (words + 7) / 8, groups = (H + 31) / 32;   // split: 256-row blocks
   const int64_t mask_bytes = words * T * 4;
   const int64_t dup_off = round_up(mask_bytes, 256);
   const int64_t d_off = dup_off + round_up(T * 4, 256);
-  const int64_t bytes = d_off + T * (wide ? H : 16) * 4;
+  int64_t bytes = d_off + T * (wide ? H : 16) * 4;
+  int64_t pre_off = 0, rank_off = 0, pds_off = 0;
+  if (wide) {
+    pre_off = round_up(bytes, 256);
+    rank_off = pre_off + round_up(blk * T * 4, 256);
+    pds_off = rank_off + round_up(T * topk * 4, 256);
+    bytes = pds_off + round_up(T * groups * topk * dsa::kDkEnt, 256) + 256;   // then the 8 queue counters
+  }
   // kv-major (H <= 16) and split (H > 16) need rows that name a large share
   // of the kv rows; both keep the prepass bitmap in LDS and the grid in 31 bits
   const bool dense = wide ? N <= 16 * (int64_t)topk : 3 * N * H <= 256 * (int64_t)topk;
-  const bool fits = words <= dsa::kKvMaxWords && bytes <= ((int64_t)1 << 30) &&
-                    (words + 1) / 2 * chunks < ((int64_t)1 << 31);
+  const int64_t wgs = wide ? 2 * blk * chunks : (words + 1) / 2 * chunks;
+  const bool fits = words <= dsa::kKvMaxWords && bytes <= ((int64_t)1 << (wide ? 36 : 30)) &&
+                    wgs < ((int64_t)1 << 31);
   if (!dense || !fits) return;
   p->schedule = wide ? DSA_BWD_SPLIT : DSA_BWD_KV_MAJOR;
   p->words = words;
   p->chunks = chunks;
+  p->blk = blk;
+  p->groups = groups;
   p->dup_off = dup_off;
   p->d_off = d_off;
+  p->pre_off = pre_off;
+  p->rank_off = rank_off;
+  p->pds_off = pds_off;
   p->ws_bytes = bytes;
 }
 
@@ -595,13 +613,25 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
     m.d_st = split ? num_heads : 16;
     m.num_words = (int32_t)plan.words;
     m.zero_dq = split ? 0 : 1;
-    const dim3 kv_grid((unsigned)((plan.words + 1) / 2 * plan.chunks));
+    m.pre = nullptr;
+    m.rank = nullptr;
+    m.pds = nullptr;
+    m.cap = topk;
+    m.groups = (int32_t)plan.groups;
+    m.num_blk = (int32_t)plan.blk;
+    m.queue = nullptr;
+    if (split) {
+      m.pre = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.pre_off);
+      m.rank = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.rank_off);
+      m.pds = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + plan.pds_off);
+      m.queue = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + plan.ws_bytes - 256);
+    }
     hipLaunchKernelGGL(dsa::sparse_mla_bwd_prep_kernel, dim3((unsigned)num_tokens), dim3(256), 0, s, a, m);
     if (split) {
-      // dkv of every token whose row repeats no entry, then dq of those
-      // tokens; the tokens with a repeated entry take the full token-major
-      // kernel (dq, and dkv with atomics)
-      hipLaunchKernelGGL(dsa::sparse_mla_bwd_kvw_kernel, kv_grid, dim3(256), 0, s, a, m);
+      // dq of every token whose row repeats no entry (which also stores P and
+      // s*dS of its entries), then dkv of those tokens from them; the tokens
+      // with a repeated entry take the full token-major kernel (dq, and dkv
+      // with atomics)
       a.only = m.dup;
       a.only_nonzero = 0;
       // dq: 64 heads per workgroup above 32 heads, else 32
@@ -614,9 +644,14 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
         hipLaunchKernelGGL(dsa::sparse_mla_bwd_dq_kernel<2>, dim3((unsigned)wgs), dim3(64 * dsa::kDqWaves), 0, s,
                            a, m);
       }
+      // persistent: one workgroup per CU (at most one fits), no more than the items
+      const int64_t dkv_wgs = std::min<int64_t>(current_device_cus(), 2 * plan.blk * plan.chunks);
+      hipLaunchKernelGGL(dsa::sparse_mla_bwd_dkv_kernel, dim3((unsigned)dkv_wgs), dim3(64 * dsa::kDkWaves), 0, s,
+                         a, m);
       a.only_nonzero = 1;
       hipLaunchKernelGGL(dsa::sparse_mla_bwd_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, s, a);
     } else {
+      const dim3 kv_grid((unsigned)((plan.words + 1) / 2 * plan.chunks));
       hipLaunchKernelGGL(dsa::sparse_mla_bwd_kv_kernel, kv_grid, dim3(256), 0, s, a, m);
       a.only = m.dup;   // rows with a repeated entry: token-major
       a.only_nonzero = 1;

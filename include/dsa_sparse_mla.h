@@ -261,14 +261,17 @@ int dsa_sparse_mla_fwd_paged_noalloc(const void* q, int64_t q_stride_tok, int64_
  * reports which one a call takes). Token-major: one workgroup per token and
  * head block adds each named row's gradient into dkv; it needs no workspace.
  * The other two serve rows that name a large share of kv (as in causal
- * prefill), when 0 < num_kv <= 262144 and their workspace is at most 1 GiB:
- *   kv-major (num_heads <= 16 and 3 * num_kv * num_heads <= 256 * topk): one
- *     workgroup per (64 kv rows, 64-token chunk) keeps the rows' dkv in
- *     registers and adds dq with atomics instead, so dq too may then differ
- *     in the last bits between calls;
- *   split (num_heads > 16 and num_kv <= 16 * topk): a kv-major pass per
- *     (64 kv rows, 256-token chunk) computes dkv, and a token-major pass
- *     computes and writes dq (no atomics on dq).
+ * prefill), when 0 < num_kv <= 262144:
+ *   kv-major (num_heads <= 16 and 3 * num_kv * num_heads <= 256 * topk,
+ *     workspace at most 1 GiB): one workgroup per (64 kv rows, 64-token
+ *     chunk) keeps the rows' dkv in registers and adds dq with atomics
+ *     instead, so dq too may then differ in the last bits between calls;
+ *   split (num_heads > 16 and num_kv <= 16 * topk, workspace at most
+ *     64 GiB): a token-major pass computes and writes dq (no atomics on dq)
+ *     and stores P and s*dS of every (token, named row) in the workspace
+ *     (topk * num_heads * 4 bytes per token, the bulk of it); a kv-major pass
+ *     per (256 kv rows, half of the columns, 256-token chunk) then forms dkv
+ *     from them.
  * Tokens whose row names some kv row twice go to the token-major kernel
  * within the same call.
  * workspace/workspace_bytes  device scratch owned by the caller, at least the

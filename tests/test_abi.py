@@ -230,7 +230,8 @@ def test_valid_call_reaches_the_device_check():
     # heads (40000 kv rows > 16 x topk) take the token-major kernel and none
     wide = dict(H=64, q_st=64 * 576, o_st=64 * 512, lse_st=64, do_st=64 * 512, dq_st=64 * 576)
     assert _bwd(**wide) == WORKSPACE
-    assert _bwd(ws=fake(8), ws_bytes=1 << 20, **wide) in (HIPERR, UNSUPPORTED)
+    assert _bwd(ws=fake(8), ws_bytes=1 << 20, **wide) == WORKSPACE   # P and s*dS: 4 MiB
+    assert _bwd(ws=fake(8), ws_bytes=1 << 23, **wide) in (HIPERR, UNSUPPORTED)
     assert _bwd(num_kv=40000, **wide) in (HIPERR, UNSUPPORTED)
 
 
@@ -256,25 +257,35 @@ def _round256(x):
     (10, 8, 0, 2048, "token-major"),           # no kv rows
 ])
 def test_bwd_workspace_query(T, H, N, topk, schedule):
-    """The schedule comes from the sizes alone, and the kv-major and split
-    workspaces are the occupancy masks, the repeat flags and D (16 heads per
-    token, or all of them above 16), each 256-byte aligned."""
+    """The schedule comes from the sizes alone. The kv-major and split
+    workspaces start with the occupancy masks, the repeat flags and D (16
+    heads per token, or all of them above 16); the split one adds the block
+    ranks (one per 256 kv rows and token), the entry ranks (topk per token)
+    P and s*dS (128 bytes per token, entry and 32-head group) and 256 bytes
+    of work-queue counters, each part 256-byte aligned."""
     got, nbytes = _bwd_ws(T, H, N, topk)
     assert got == schedule
-    if schedule != "token-major":
-        words = (N + 31) // 32
-        assert nbytes == _round256(words * T * 4) + _round256(T * 4) + T * max(H, 16) * 4
+    words = (N + 31) // 32
+    base = _round256(words * T * 4) + _round256(T * 4) + T * max(H, 16) * 4
+    if schedule == "kv-major":
+        assert nbytes == base
+    elif schedule == "split":
+        blk, groups = (words + 7) // 8, (H + 31) // 32
+        assert nbytes == (_round256(base) + _round256(blk * T * 4) + _round256(T * topk * 4)
+                          + _round256(T * groups * topk * 128) + 256)   # then the dkv queue counters
     else:
         assert nbytes == 0
 
 
 def test_bwd_workspace_cap():
-    """Above 1 GiB of masks the token-major schedule runs instead."""
+    """Above 1 GiB of kv-major workspace, or 64 GiB of split workspace, the
+    token-major schedule runs instead."""
     T, N = 65536, 131072   # 4096 words x 65536 tokens x 4 bytes = 1 GiB of masks alone
     assert _bwd_ws(T, 1, N, 65536)[0] == "token-major"
     assert _bwd_ws(T // 2, 1, N, 65536)[0] == "kv-major"
-    assert _bwd_ws(T, 64, N, 65536)[0] == "token-major"
-    assert _bwd_ws(T // 2, 64, N, 65536)[0] == "split"
+    # 64 heads: P and s*dS take 256 bytes per (token, entry); 65536 x 2048 is 32 GiB
+    assert _bwd_ws(65536, 64, 32768, 2048)[0] == "split"
+    assert _bwd_ws(131072, 64, 32768, 2048)[0] == "token-major"   # 64 GiB and more
 
 
 def test_bwd_workspace_query_rejects_bad_sizes():

@@ -55,7 +55,7 @@ def test_source_hash_per_op(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     before = {op: bench.source_hash(op) for op in ("fwd", "bwd", "topk")}
     full = bench.source_hash()
-    (csrc / "bwd_kvw_kernel.hpp").write_text("changed")
+    (csrc / "bwd_dkv_kernel.hpp").write_text("changed")
     after = {op: bench.source_hash(op) for op in ("fwd", "bwd", "topk")}
     assert after["fwd"] == before["fwd"] and after["topk"] == before["topk"]
     assert after["bwd"] != before["bwd"] and bench.source_hash() != full
@@ -171,7 +171,7 @@ def test_counter_summary_per_kernel(tmp_path):
         w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
         w.writeheader()
         for disp, k, busy, mfma in ((1, "dsa::dkv_zero_kernel(float*, long, long)", 3200, 0),
-                                    (2, "dsa::sparse_mla_bwd_kvw_kernel(dsa::BwdArgs, dsa::KvMajorArgs)", 320000, 2048000),
+                                    (2, "dsa::sparse_mla_bwd_dkv_kernel(dsa::BwdArgs, dsa::KvMajorArgs)", 320000, 2048000),
                                     (3, "dsa::sparse_mla_bwd_dq_kernel(dsa::BwdArgs, dsa::KvMajorArgs)", 160000, 512000)):
             w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "SQ_BUSY_CYCLES", "Counter_Value": busy})
             w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES",
@@ -179,6 +179,6 @@ def test_counter_summary_per_kernel(tmp_path):
     args = argparse.Namespace(op="bwd", workload="wide", traffic_command="cmd")
     bench.summarize_counters(args, [str(p)], out_dir=str(tmp_path))
     out = json.load(open(tmp_path / "counters_bwd_wide.json"))
-    assert "kvw" in out["kernel"] and out["mfma_busy_frac"] == 0.2   # 2048000 / (1024 * 320000 / 32)
+    assert "dkv_kernel" in out["kernel"] and out["mfma_busy_frac"] == 0.2   # 2048000 / (1024 * 320000 / 32)
     assert len(out["per_kernel"]) == 3
     assert out["per_kernel"]["dsa::sparse_mla_bwd_dq_kernel(dsa::BwdArgs, dsa::KvMajorArgs)"]["mfma_busy_frac"] == 0.1
