@@ -18,7 +18,6 @@
 //   phase 3: wave w: dq column tiles 4k + w (k = 0..8) of both head tiles
 //            += (s dS) K, K^T read transposed from the stage.
 // Two barriers per tile: after phase 2, and once the next tile has landed.
-// D = dO . O comes from the prepass (one value per token and head).
 //
 // Pages: "[Feature] Add optional FlashMLA backend for DSA Sparse MLA"
 // (xtuner PR 2083), Motivation (forward output and LSE feed the backward);
@@ -160,8 +159,23 @@ sparse_mla_bwd_dq_kernel(const BwdArgs a, const KvMajorArgs m) {
         bdo[c] = head_ok ? v : (bf16x8_t){};
       }
     }
-    // D from the prepass; LSE in log2 units, +inf for padded heads (P = 0 there)
-    const float Dh = head_ok ? m.dbuf[token * m.d_st + head] : 0.f;
+    // D = dO . O of the lane's head, with dO from the operand registers (the
+    // four lanes of a head hold its 512 columns); LSE in log2 units, +inf
+    // for padded heads (P = 0 there)
+    float Dh;
+    {
+      const uint16_t* op = a.out + token * a.o_st + (int64_t)(head_ok ? head : 0) * a.o_sh + 8 * g;
+      float d = 0.f;
+#pragma unroll
+      for (int c = 0; c < kDv / 32; ++c) {
+        const bf16x8_t o = *(const bf16x8_t*)(op + 32 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d += (float)o[e] * (float)bdo[c][e];
+      }
+      d += __shfl_xor(d, 16);
+      d += __shfl_xor(d, 32);
+      Dh = head_ok ? d : 0.f;
+    }
     const float l2 = head_ok ? a.lse[token * a.lse_st + head] * 1.4426950408889634f : INFINITY;
     // P and s dS for the dkv pass: after the quad transpose, lane (g, n)
     // holds key 16kb + 4g + (n & 3) and heads 16ht + 4(n >> 2) .. +3; they go

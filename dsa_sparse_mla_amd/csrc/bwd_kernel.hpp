@@ -423,8 +423,8 @@ constexpr int kKvMaxWords = 8192;   // mask words per token row held in LDS (kv 
 struct KvMajorArgs {
   uint32_t* mask;     // u32 [num_words][num_tokens]: word w of token t at mask[w * T + t]
   uint32_t* dup;      // u32 [num_tokens]: 1 = the row names a kv row twice
-  float* dbuf;        // fp32 [num_tokens][d_st]: D = dO . O per head (0 past num_heads)
-  int64_t d_st;       // heads per token row of dbuf: 16, or num_heads above 16
+  float* dbuf;        // fp32 [num_tokens][16]: D = dO . O per head (0 past num_heads); null: not formed
+  int64_t d_st;       // heads per token row of dbuf (16)
   int32_t num_words;  // ceil(num_kv / 32)
   int32_t zero_dq;    // 1: the prepass zeroes dq (the kv-major pass adds into it)
   // Split schedule only (null otherwise). A token's named rows, ordered by
@@ -459,8 +459,9 @@ sparse_mla_bwd_prep_kernel(const BwdArgs a, const KvMajorArgs m) {
       if (atomicOr(&s_bm[v >> 5], bit) & bit) s_dup = 1u;
     }
   }
-  // D per head (wave w: heads w, w + 4, ..) and, for the kv-major pass, dq = 0
-  for (int h = wave; h < m.d_st; h += 4) {
+  // D per head (wave w: heads w, w + 4, ..; the kv-major pass only: the
+  // split schedule's dq pass forms D itself) and, for the kv-major pass, dq = 0
+  for (int h = wave; m.dbuf != nullptr && h < m.d_st; h += 4) {
     float d = 0.f;
     if (h < a.num_heads) {
       const bf16x8_t o = *(const bf16x8_t*)(a.out + token * a.o_st + (int64_t)h * a.o_sh + 8 * lane);

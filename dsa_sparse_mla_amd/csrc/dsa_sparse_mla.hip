@@ -204,7 +204,7 @@ void bwd_plan(int64_t T, int32_t H, int64_t N, int32_t topk, BwdPlan* p) {
   const int64_t mask_bytes = words * T * 4;
   const int64_t dup_off = round_up(mask_bytes, 256);
   const int64_t d_off = dup_off + round_up(T * 4, 256);
-  int64_t bytes = d_off + T * (wide ? H : 16) * 4;
+  int64_t bytes = d_off + (wide ? 0 : T * 16 * 4);   // D: kv-major only (the split dq pass forms it)
   int64_t pre_off = 0, rank_off = 0, pds_off = 0;
   if (wide) {
     pre_off = round_up(bytes, 256);
@@ -609,8 +609,8 @@ int dsa_sparse_mla_bwd(const void* q, int64_t q_stride_tok, int64_t q_stride_hea
     dsa::KvMajorArgs m;
     m.mask = static_cast<uint32_t*>(workspace);
     m.dup = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + plan.dup_off);
-    m.dbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.d_off);
-    m.d_st = split ? num_heads : 16;
+    m.dbuf = split ? nullptr : reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.d_off);
+    m.d_st = 16;
     m.num_words = (int32_t)plan.words;
     m.zero_dq = split ? 0 : 1;
     m.pre = nullptr;

@@ -258,15 +258,15 @@ def _round256(x):
 ])
 def test_bwd_workspace_query(T, H, N, topk, schedule):
     """The schedule comes from the sizes alone. The kv-major and split
-    workspaces start with the occupancy masks, the repeat flags and D (16
-    heads per token, or all of them above 16); the split one adds the block
+    workspaces start with the occupancy masks and the repeat flags, then the
+    kv-major one holds D (16 heads per token); the split one adds the block
     ranks (one per 256 kv rows and token), the entry ranks (topk per token)
     P and s*dS (128 bytes per token, entry and 32-head group) and 256 bytes
     of work-queue counters, each part 256-byte aligned."""
     got, nbytes = _bwd_ws(T, H, N, topk)
     assert got == schedule
     words = (N + 31) // 32
-    base = _round256(words * T * 4) + _round256(T * 4) + T * max(H, 16) * 4
+    base = _round256(words * T * 4) + _round256(T * 4) + (T * 16 * 4 if H <= 16 else 0)
     if schedule == "kv-major":
         assert nbytes == base
     elif schedule == "split":
