@@ -6,7 +6,8 @@ synchronisation, no memset node), so it can be captured. The test captures
 one call with preallocated outputs, replays the graph several times with
 eager work on the same buffers between the replays, and requires every
 replay to equal the eager result bit for bit (and the eager result to match
-the oracle at the forward's tolerance).
+the oracle at the forward's tolerance); the backward's atomically summed
+outputs are held to a bound instead (see its test).
 """
 from __future__ import annotations
 
@@ -15,7 +16,7 @@ import pytest
 import torch
 
 import workloads
-from oracle import sparse_mla_fwd_paged_ref, sparse_mla_fwd_ref, topk_indices_ref
+from oracle import sparse_mla_bwd_ref, sparse_mla_fwd_paged_ref, sparse_mla_fwd_ref, topk_indices_ref
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -122,3 +123,49 @@ def test_topk_captured():
         assert torch.equal(rep[0], eager[0])
     want = topk_indices_ref(scores.cpu().numpy(), ks.cpu().numpy(), ke.cpu().numpy(), 256)
     assert np.array_equal(eager[0].cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("H", [8, 64])
+def test_backward_captured(H):
+    """The backward under capture (8 heads: the kv-major schedule; 64: the
+    split one). Between replays the outputs and the whole workspace are
+    overwritten, so every part a call reads (masks, ranks, P and s*dS, the
+    dkv pass's work-queue counters) must be rebuilt inside the captured call.
+    The split schedule's dq is written by one workgroup per token and must
+    equal the eager result bit for bit; dkv (and the kv-major dq) are sums
+    of atomic adds whose order may change from call to call, so they must
+    agree to 1e-5 of the tensor's largest magnitude. The eager result is
+    checked against the oracle (Frobenius error within 1e-2, the backward
+    tests' end-to-end bound: out and LSE come from the library's forward)."""
+    dsa = _dsa()
+    T, N, topk, sm = 300, 200, 160, 1 / 24
+    rng = np.random.default_rng(83 + H)
+    g = torch.Generator().manual_seed(83 + H)
+    q = torch.randn((T, H, 576), generator=g).to(torch.bfloat16)
+    kv = torch.randn((N, 576), generator=g).to(torch.bfloat16)
+    dout = torch.randn((T, H, 512), generator=g).to(torch.bfloat16)
+    idx = np.stack([rng.permutation(N)[:topk] for _ in range(T)]).astype(np.int32)
+    idx[rng.random((T, topk)) < 0.3] = -1
+    qd, kd, idd, dod = q.to(DEV), kv.to(DEV), torch.from_numpy(idx).to(DEV), dout.to(DEV)
+    out, lse = dsa.sparse_mla_fwd(qd, kd, idd, sm)
+    sched, nbytes = dsa.bwd_workspace_size(T, H, N, topk)
+    assert sched == ("kv-major" if H == 8 else "split")
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    dq = torch.empty((T, H, 576), dtype=torch.float32, device=DEV)
+    dkv = torch.empty((N, 576), dtype=torch.float32, device=DEV)
+
+    def fn():
+        dsa.sparse_mla_bwd(qd, kd, idd, sm, out, lse, dod, dq=dq, dkv=dkv, workspace=ws)
+
+    eager, got = _replays(fn, [dq, dkv, ws])
+    for rep in got:
+        for i in range(2):
+            a, b = rep[i], eager[i]
+            if i == 0 and sched == "split":
+                assert torch.equal(a, b)
+            else:
+                assert torch.allclose(a, b, rtol=0.0, atol=1e-5 * float(b.abs().max()))
+    rdq, rdkv = sparse_mla_bwd_ref(q.double().numpy(), kv.double().numpy(), idx, sm, dout.double().numpy())
+    for x, r in ((eager[0], rdq), (eager[1], rdkv)):
+        x = x.double().cpu().numpy()
+        assert np.linalg.norm(x - r) <= 1e-2 * np.linalg.norm(r)
