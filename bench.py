@@ -9,9 +9,10 @@ dqk 576 / dv 512, topk 2048, bf16 (the shape of "feat: add XTuner TileLang
 sparse MLA backend", Performance > Isolated sparse MLA forward).
 
 With --op bwd it times the backward instead (flat workloads): one step is
-one backward call (the dkv zero fill, then the token-major kernel, or the
-kv-major prepass and pass with the token-major kernel for rows that repeat
-an entry), after one forward that supplies out and LSE; `value` then counts
+one backward call (the dkv zero fill, then the token-major kernel; or the
+prepass, the kv-major pass (up to 16 heads) or the split schedule's dq and
+dkv passes, and the token-major kernel for rows that repeat an entry), after
+one forward that supplies out and LSE; `value` then counts
 the 1152-byte gathered row per valid key, as for the forward, and `tflops`
 5504 flops per valid key and head.
 
@@ -91,8 +92,9 @@ def traffic_for(workload: str, op: str = "fwd"):
 
 COPY_BYTES = 256 << 20   # the calibration copy reads and writes this many bytes
 FWD_KERNEL = re.compile(r"sparse_mla_fwd(_ws)?_kernel")   # the forward kernels' names
-# the kernels of one backward call: the dkv fill (once per call), the kv-major
-# prepass and pass, and the token-major kernel
+# the kernels of one backward call: the dkv fill (once per call), the
+# prepass, the kv-major pass or the split schedule's dq and dkv passes, and
+# the token-major kernel
 BWD_KERNEL = re.compile(r"dkv_zero_kernel|sparse_mla_bwd_(prep_|kv_|dkv_|dq_)?kernel")
 BWD_CALL_MARK = re.compile(r"dkv_zero_kernel")
 TOPK_KERNEL = re.compile(r"topk_select_kernel")

@@ -1,23 +1,29 @@
 // dq pass of the split backward schedule (more than 16 heads): for every
 // token whose index row repeats no entry, dq = s dS K over the token's valid
-// keys (the notation of bwd_kernel.hpp); the dkv pass (bwd_kvw_kernel.hpp)
-// produces dkv of the same tokens.
+// keys (the notation of bwd_kernel.hpp), and P and s dS of every (key, head)
+// stored for the dkv pass (bwd_dkv_kernel.hpp), which forms dkv of the same
+// tokens from them.
 //
-// One workgroup of 4 waves = (token, block of 32 heads). The index row is
-// compacted per 2048-entry segment as in the forward, into the named row
-// ids. Tiles of 32 keys are copied HBM -> LDS with global_load_lds_dwordx4
-// into a ring of four stages, three tiles ahead of the one in use, in the
-// token-major kernel's stage layout (swizzled latent and rope parts). Per
-// tile:
-//   phase 1: wave w = (key block kb = w & 1, head tile ht = w >> 1) forms
-//            S^T = K Q^T and dP^T = V dO^T of its 16 keys x 16 heads
-//            (16x16x32 MFMA, Q^T and dO^T in registers); each K-row read
-//            feeds both products;
-//   phase 2: the same wave: P = exp(s S - LSE) and s dS = s P (dP - D), into
-//            LDS as bf16 [head][32 keys] in phase 3's k-slot order;
-//   phase 3: wave w: dq column tiles 4k + w (k = 0..8) of both head tiles
-//            += (s dS) K, K^T read transposed from the stage.
-// Two barriers per tile: after phase 2, and once the next tile has landed.
+// One workgroup of 8 waves = (token, block of 64 heads; 32 at up to 32
+// heads), two waves per SIMD with split roles. The index row is compacted
+// per 2048-entry segment as in the forward, into the named row ids. Tiles
+// of 32 keys are copied HBM -> LDS with global_load_lds_dwordx4 by the dq
+// waves into a ring of four stages (swizzled latent and rope parts). Per
+// tile j:
+//   S waves (4): wave w forms S^T = K Q^T and dP^T = V dO^T of head tile w
+//            over both 16-key blocks (at 32 heads: key block w & 1 of head
+//            tile w >> 1) on 16x16x32 MFMA, with Q^T and dO^T in registers
+//            and each K-row read feeding both products; then P = exp(s S -
+//            LSE) and s dS = s P (dP - D) (D = dO . O, formed once per token
+//            from O and the dO registers), s dS into LDS as bf16 [head][32
+//            keys] in the dq product's k-slot order, and P and s dS
+//            transposed over lane quads into per-key rows, stored at each
+//            key's rank (read from the prepass one tile ahead) during the
+//            next tile's products;
+//   dq waves (4): dq column tiles 4k + w (k = 0..8) of every head tile +=
+//            (s dS) K for tile j - 1, K^T read transposed from the stage,
+//            and the copies of tile j + 2.
+// One barrier per tile (s dS of tile j written; tile j + 1 landed).
 //
 // Pages: "[Feature] Add optional FlashMLA backend for DSA Sparse MLA"
 // (xtuner PR 2083), Motivation (forward output and LSE feed the backward);

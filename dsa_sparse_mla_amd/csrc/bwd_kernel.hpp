@@ -72,7 +72,7 @@ constexpr int kBwPitch = 1168;                  // LDS row pitch of Q rows (and 
 constexpr int kBwLat = kTileKeys * kDv * 2;     // stage of one tile: the 32 latent parts (1024 B each),
 constexpr int kBwStage = kBwLat + kTileKeys * (kDqk - kDv) * 2;   // then the 32 rope parts (128 B each)
 
-// Swizzles of the stage and of the dkv pass's step buffers: granule G (16 B)
+// Swizzles of the key stages (token-major kernel and dq pass): granule G (16 B)
 // of the latent part of row r sits at G ^ bw_swz(r) within its 256-byte
 // group, rope granule G at G ^ bw_swz_r(r). Chosen by measurement
 // (SQ_LDS_BANK_CONFLICT on probes of both read patterns): the transposed

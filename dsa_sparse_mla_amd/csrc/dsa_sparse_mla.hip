@@ -182,10 +182,12 @@ void* scratch_address(int dev) {
 // at 16, 4.7x on packed documents at 8 heads. Its workspace holds the
 // per-token occupancy masks ([word][token] u32), the per-token repeat flags
 // and D = dout . out per (token, head); above 1 GiB of it the token-major
-// kernel runs instead. The split schedule's workspace adds the prepass's
-// ranks (per 256-row block and per index entry) and the dq pass's P and
-// s*dS, 128 bytes per (token, entry, 32-head group): topk x H x 4 bytes per
-// token. Above 64 GiB of it the token-major kernel runs instead.
+// kernel runs instead. The split schedule (more than 16 heads, num_kv at most
+// 16 topk) keeps the masks and flags (its dq pass forms D itself) and adds
+// the prepass's ranks (per 256-row block and per index entry), the dq pass's
+// P and s*dS, 128 bytes per (token, entry, 32-head group): topk x H x 4
+// bytes per token, and the dkv pass's 8 work-queue counters. Above 64 GiB of
+// it the token-major kernel runs instead.
 struct BwdPlan {
   int schedule = DSA_BWD_TOKEN_MAJOR;
   int64_t words = 0, chunks = 0, blk = 0, groups = 0;
