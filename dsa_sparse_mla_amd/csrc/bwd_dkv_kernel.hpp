@@ -12,7 +12,7 @@
 // the popcount of the token's mask words over the block), so the pass copies
 // that run.
 //
-// One work item = (256 kv rows r0 .., column half ch, chunk of 256 tokens):
+// One work item = (256 kv rows r0 .., column half ch, chunk of 64 tokens):
 // latent columns 256ch .. 256ch+255 and rope columns 512 + 32ch .. +31. It
 // collects the chunk's tokens whose masks name any of its rows and takes
 // them in steps of one token and one head group. A step has two parts, each
@@ -58,7 +58,9 @@ namespace dsa {
 
 constexpr int kDkRows = 256;                      // kv rows per work item (eight mask words)
 constexpr int kDkWords = kDkRows / 32;
-constexpr int kDkChunk = 256;                     // tokens per work item (four ballots of 64)
+constexpr int kDkChunk = 64;                      // tokens per work item (one ballot)
+constexpr int kDkBallots = kDkChunk / 64;
+static_assert(kDkChunk % 64 == 0 && kDkBallots <= 4, "waves 0 .. kDkBallots-1 collect the chunk's tokens");
 constexpr int kDkWaves = 8;
 constexpr int kDkHeads = 32;                      // heads per step (one head group)
 constexpr int kDkQR = kDkHeads * 512;             // rope rows within a q part
@@ -100,8 +102,10 @@ __device__ __forceinline__ void dk_wait(int nl) {
 // and half by half, so that the XCD's workgroups take one chunk's items
 // together and read each token's q and dO at about the same time (from that
 // XCD's L2). A workgroup whose queue is empty takes items from the next
-// queues. Counters start at 0 (the prepass clears them); each ends past its
-// queue's length, so every workgroup leaves the loop.
+// queues. Short items (64 tokens) keep the last round short: with 256-token
+// items the last of them ran alone for about a sixth of the pass. Counters
+// start at 0 (the prepass clears them); each ends past its queue's length,
+// so every workgroup leaves the loop.
 __global__ void __launch_bounds__(64 * kDkWaves)
 sparse_mla_bwd_dkv_kernel(const BwdArgs a, const KvMajorArgs m) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_part[kDkParts][kDkPart];
@@ -155,7 +159,7 @@ sparse_mla_bwd_dkv_kernel(const BwdArgs a, const KvMajorArgs m) {
     uint32_t w[kDkWords];
     uint64_t act = 0;
     const int64_t t = t0 + 64 * wave + lane;
-    if (wave < 4) {
+    if (wave < kDkBallots) {
       uint32_t any = 0u;
 #pragma unroll
       for (int i = 0; i < kDkWords; ++i) {
@@ -166,7 +170,7 @@ sparse_mla_bwd_dkv_kernel(const BwdArgs a, const KvMajorArgs m) {
       if (lane == 0) s_wcnt[wave] = __popcll(act);
     }
     __syncthreads();
-    if (wave < 4 && ((act >> lane) & 1ull)) {
+    if (wave < kDkBallots && ((act >> lane) & 1ull)) {
       int base = 0;
       for (int i = 0; i < wave; ++i) base += s_wcnt[i];
       const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(act >> 32),
@@ -177,7 +181,9 @@ sparse_mla_bwd_dkv_kernel(const BwdArgs a, const KvMajorArgs m) {
       s_pre[pos] = m.pre[(int64_t)blk * T + t];
     }
   }
-  const int np = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+  int np = 0;
+#pragma unroll
+  for (int i = 0; i < kDkBallots; ++i) np += s_wcnt[i];
   if (np == 0) continue;   // uniform over the workgroup
   __syncthreads();
 

@@ -270,7 +270,7 @@ int dsa_sparse_mla_fwd_paged_noalloc(const void* q, int64_t q_stride_tok, int64_
  *     64 GiB): a token-major pass computes and writes dq (no atomics on dq)
  *     and stores P and s*dS of every (token, named row) in the workspace
  *     (topk * num_heads * 4 bytes per token, the bulk of it); a kv-major pass
- *     per (256 kv rows, half of the columns, 256-token chunk) then forms dkv
+ *     per (256 kv rows, half of the columns, 64-token chunk) then forms dkv
  *     from them.
  * Tokens whose row names some kv row twice go to the token-major kernel
  * within the same call.

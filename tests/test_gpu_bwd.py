@@ -354,7 +354,7 @@ def split(H, N, topk, T=64):
 
 @pytest.mark.parametrize("H", [17, 32, 33, 64, 128])
 def test_bwd_split_schedule(H):
-    """The split schedule: 300 tokens (two 256-token chunks of the dkv pass,
+    """The split schedule: 300 tokens (five 64-token chunks of the dkv pass,
     the last ragged), 200 kv rows (one 256-row block that runs past them),
     distinct entries with -1 and out-of-range values; a token with no key, a
     token with only out-of-range values, and two tokens that name a row twice
