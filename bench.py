@@ -501,14 +501,23 @@ def time_steps(step, steps: int, warmup: int, stream):
     return sum(ms) / len(ms), ms[len(ms) // 2], wall * 1e3 / steps
 
 
-def time_flushed(step, steps: int, dev, stream):
+def time_flushed(step, steps: int, dev, stream, dirty: bool = False):
     """Median event ms of launches that each start with no KV in L2 or the
-    MALL: a 512 MB write between launches, outside the events."""
+    MALL. Between launches, outside the events, a 512 MB write evicts the
+    caches, and a read of another 512 MB then evicts the written lines, so
+    their write-back to HBM happens before the launch and the caches hold
+    clean, unrelated lines. With dirty=True the read is left out: the launch
+    then starts with the L2s and the MALL full of dirty lines and pays their
+    write-back inside the events (the cold case behind a writing kernel)."""
     import torch
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    clean = None if dirty else torch.ones(128 << 20, dtype=torch.int32, device=dev)
     fl = []
     for i in range(steps):
         scratch.fill_(i & 255)
+        if clean is not None:
+            clean.sum()
+        torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -516,7 +525,7 @@ def time_flushed(step, steps: int, dev, stream):
         e1.record(stream)
         torch.cuda.synchronize()
         fl.append(e0.elapsed_time(e1))
-    del scratch
+    del scratch, clean
     fl.sort()
     return fl[len(fl) // 2]
 
@@ -574,6 +583,9 @@ def fwd_leg(name: str, dev, stream, steps: int, warmup: int, flush: bool):
         rec["kernel_ms_flushed"] = round(fl, 5)
         rec["gathered_kv_gbps_flushed"] = round(gathered / (fl * 1e-3) / 1e9, 1)
         rec["hbm_frac_flushed"] = round(rec["gathered_kv_gbps_flushed"] / HBM_PEAK_GBPS, 4)
+        fd = time_flushed(f["step"], steps, dev, stream, dirty=True)
+        rec["kernel_ms_flushed_dirty"] = round(fd, 5)
+        rec["hbm_frac_flushed_dirty"] = round(gathered / (fd * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
     t = traffic_for(name)
     if t is not None:
         rec["hbm_traffic_bytes"] = t
@@ -649,8 +661,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 skips it)")
     ap.add_argument("--flush", action="store_true",
-                    help="also time launches with a 512 MB scratch write between them (caches cold), "
-                         "reported as kernel_ms_flushed")
+                    help="also time launches with cold caches: kernel_ms_flushed after a 512 MB write "
+                         "and a 512 MB read between launches (clean caches), kernel_ms_flushed_dirty "
+                         "after the write alone (its dirty lines are written back inside the launch)")
     ap.add_argument("--no-legs", action="store_true",
                     help="fwd only: skip the wide-head and flushed-decode legs (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -748,6 +761,7 @@ def main():
         copy_calibration(dev)
     avg_ms, med_ms, ms_per_step = time_steps(step, args.steps, args.warmup, stream)
     flushed_ms = time_flushed(step, args.steps, dev, stream) if args.flush else None
+    flushed_dirty_ms = time_flushed(step, args.steps, dev, stream, dirty=True) if args.flush else None
 
     if args.op == "bwd":
         gathered = V * BWD_BYTES_PER_KEY
@@ -796,7 +810,8 @@ def main():
         "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 3),
         "roofline": roof,
         **({"kernel_ms_flushed": round(flushed_ms, 5),
-            "gathered_kv_gbps_flushed": round(gathered / (flushed_ms * 1e-3) / 1e9, 2)}
+            "gathered_kv_gbps_flushed": round(gathered / (flushed_ms * 1e-3) / 1e9, 2),
+            "kernel_ms_flushed_dirty": round(flushed_dirty_ms, 5)}
            if flushed_ms is not None else {}),
         "source_hash": source_hash(args.op),
     }
