@@ -52,6 +52,7 @@ constexpr int kTkThreads = 512;
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kTkCache = 16384;   // candidate keys held in LDS (64 KB)
 constexpr int kTkPer = 8;         // consecutive columns per thread in a chunk
+constexpr int kTkCopies = 8;      // copies of each histogram bin (lane & 7 picks one)
 constexpr int kTkChunk = kTkThreads * kTkPer;   // columns per chunk (4096)
 static_assert(kTkCache % kTkChunk == 0, "cached rows end on a chunk boundary");
 
@@ -65,6 +66,8 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+__device__ __forceinline__ uint32_t hist_at(uint32_t b, uint32_t c) { return 256u * c + ((b + 8u * c) & 255u); }
+
 // lanes below this one whose bit is set in m
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -72,7 +75,10 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 
 __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs a) {
   __shared__ uint32_t s_key[kTkCache];
-  __shared__ uint32_t s_hist[kTkWaves][256];
+  // copy c of bin b at s_hist[hist_at(b, c)]: the copies of one bin fall in
+  // eight different banks, and the 64 bins 4l + i that wave 0's lanes read
+  // for one (i, c) spread over 16 banks
+  __shared__ uint32_t s_hist[256 * kTkCopies];
   __shared__ uint32_t s_wsum[2][kTkWaves];
   __shared__ uint32_t s_state[2];   // next byte's digit, keys still to take from it
 
@@ -100,14 +106,18 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
   // indices past the row are clamped to its last column (the caller masks
   // them), so the loads are issued together. From LDS they are keys; from
   // the scores, raw score bits that to_key turns into keys when used.
+  // Offsets are 32-bit: the host caps num_cols at INT32_MAX, so n - 1 and
+  // j0 + i * stride (below n + kTkPer * kTkThreads) fit.
+  const uint32_t last = (uint32_t)(n - 1);
   auto load_raw = [&](auto lds_tag, int64_t j0, int64_t stride, uint32_t* raw) {
+    const uint32_t b = (uint32_t)j0, st = (uint32_t)stride;
     if constexpr (decltype(lds_tag)::value) {
 #pragma unroll
-      for (int i = 0; i < kTkPer; ++i) raw[i] = s_key[min(j0 + i * stride, n - 1)];
+      for (int i = 0; i < kTkPer; ++i) raw[i] = s_key[min(b + i * st, last)];
     } else {
       const uint32_t* sr = reinterpret_cast<const uint32_t*>(srow);
 #pragma unroll
-      for (int i = 0; i < kTkPer; ++i) raw[i] = sr[min(j0 + i * stride, n - 1)];
+      for (int i = 0; i < kTkPer; ++i) raw[i] = sr[min(b + i * st, last)];
     }
   };
   auto to_key = [](auto lds_tag, uint32_t raw) {
@@ -117,12 +127,18 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
 
   // ---------------------------------------------------------------- 1. radix select
   // Two barriers per pass: counts complete, then the chosen digit published.
-  // Each wave counts into its own histogram row and clears it itself after
-  // the second barrier (wave 0 reads every row before that barrier).
+  // Lane l counts into copy l & 7 of each bin: scores concentrate in a few
+  // values of the top byte, and one copy per bin would serialise most of a
+  // wave's atomics on a handful of addresses. The copies are shared by all
+  // waves, so only wave 0 touches them between the two barriers: it reads
+  // each count and writes 0 back, which leaves the histogram clear for the
+  // next pass.
   uint32_t prefix = 0, mask = 0;
   uint32_t remaining = (uint32_t)k;
+  const uint32_t copy = (uint32_t)lane & (kTkCopies - 1);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s_hist[wave][4 * lane + i] = 0u;
+  for (int i = 0; i < 4; ++i) s_hist[256 * wave + 64 * i + lane] = 0u;
+  __syncthreads();   // clear before any wave counts
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     // kTkPer keys per thread and round; the next round's entries are
@@ -141,7 +157,7 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
           const int64_t j = j0 + (int64_t)i * kTkThreads;
           if (j < n) {
             if (pass == 0 && cached) s_key[j] = key[i];
-            if (((key[i] ^ prefix) & mask) == 0u) atomicAdd(&s_hist[wave][(key[i] >> shift) & 255u], 1u);
+            if (((key[i] ^ prefix) & mask) == 0u) atomicAdd(&s_hist[hist_at((key[i] >> shift) & 255u, copy)], 1u);
           }
         }
       }
@@ -153,11 +169,18 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
       // lane l takes bins 4l .. 4l+3: their totals over the waves, the keys
       // in higher bins (a suffix sum over the lanes), then the bin where the
       // count from the top reaches `remaining`
+      // copy cp of bins 4l .. 4l+3 is four consecutive words (16-byte aligned)
       uint32_t c[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int w = 0; w < kTkWaves; ++w)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) c[i] += s_hist[w][4 * lane + i];
+      for (int cp = 0; cp < kTkCopies; ++cp) {
+        uint4* w = reinterpret_cast<uint4*>(&s_hist[hist_at(4 * lane, cp)]);
+        const uint4 v = *w;
+        *w = make_uint4(0u, 0u, 0u, 0u);
+        c[0] += v.x;
+        c[1] += v.y;
+        c[2] += v.z;
+        c[3] += v.w;
+      }
       const uint32_t tot = (c[0] + c[1]) + (c[2] + c[3]);
       uint32_t incl = tot;
 #pragma unroll
@@ -175,12 +198,10 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
         above += c[i];
       }
     }
-    __syncthreads();   // the digit is published; wave 0 is done reading the counts
+    __syncthreads();   // the digit is published; the histogram is clear again
     prefix |= s_state[0] << shift;
     mask |= 255u << shift;
     remaining = s_state[1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_hist[wave][4 * lane + i] = 0u;   // this wave's row, for the next pass
   }
   const uint32_t K = prefix;    // the k-th key; `remaining` keys equal to it are taken
 
