@@ -207,9 +207,11 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
 
   // ---------------------------------------------------------------- 2. ordered compaction
   // Chunks of kTkChunk columns; thread tid takes columns kTkPer tid .. +kTkPer-1
-  // of the chunk, so thread order is column order. Two workgroup prefix
-  // counts per chunk: the keys equal to K before each column, then the
-  // selected columns before each. The next chunk's keys are loaded first.
+  // of the chunk, so thread order is column order. One workgroup prefix count
+  // per chunk, of the pair (keys > K, keys == K) packed in one word (each at
+  // most kTkChunk): a column's place is the keys > K before it plus the keys
+  // == K before it, capped at `remaining` (the first of those are taken). The
+  // next two chunks' keys are in flight.
   // Exclusive prefix of v over the threads and its total (s_wsum[buf]).
   auto wg_scan = [&](uint32_t v, int buf, uint32_t& total) -> uint32_t {
     uint32_t incl = v;
@@ -230,43 +232,51 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
     }
     return before;
   };
+  static_assert(kTkChunk < 65536, "both counts of a chunk fit 16 bits");
   auto load_chunk = [&](auto lds_tag, int64_t c0, uint32_t* raw) { load_raw(lds_tag, c0 + (int64_t)kTkPer * tid, 1, raw); };
-  uint32_t eq_base = 0, sel_base = 0;
+  uint32_t gt_base = 0, eq_base = 0;
+  auto taken = [&] { return gt_base + min(eq_base, remaining); };   // columns placed so far
   auto compact = [&](auto lds_tag) {
-    uint32_t cur[kTkPer], nxt[kTkPer];
+    // chunks c+1 and c+2 are in flight while chunk c is placed
+    uint32_t cur[kTkPer], nxt[kTkPer], nxt2[kTkPer];
     load_chunk(lds_tag, 0, cur);
-    for (int64_t c0 = 0; c0 < n && sel_base < (uint32_t)k; c0 += kTkChunk) {
+    if (kTkChunk < n) load_chunk(lds_tag, kTkChunk, nxt);
+    int buf = 0;
+    for (int64_t c0 = 0; c0 < n && taken() < (uint32_t)k; c0 += kTkChunk) {
 #pragma unroll
       for (int i = 0; i < kTkPer; ++i) cur[i] = to_key(lds_tag, cur[i]);
-      if (c0 + kTkChunk < n) load_chunk(lds_tag, c0 + kTkChunk, nxt);
+      if (c0 + 2 * kTkChunk < n) load_chunk(lds_tag, c0 + 2 * kTkChunk, nxt2);
       const int64_t jt = c0 + (int64_t)kTkPer * tid;   // this thread's first column
-      uint32_t neq = 0;
+      uint32_t ngt = 0, neq = 0;
 #pragma unroll
-      for (int i = 0; i < kTkPer; ++i) neq += (jt + i < n && cur[i] == K) ? 1u : 0u;
-      uint32_t eq_all, sel_all;
-      uint32_t e = eq_base + wg_scan(neq, 0, eq_all);
-      bool sel[kTkPer];
-      uint32_t nsel = 0;
+      for (int i = 0; i < kTkPer; ++i) {
+        const bool in = jt + i < n;
+        ngt += (in && cur[i] > K) ? 1u : 0u;
+        neq += (in && cur[i] == K) ? 1u : 0u;
+      }
+      uint32_t all;
+      const uint32_t before = wg_scan((ngt << 16) | neq, buf, all);   // chunks alternate buffers
+      buf ^= 1;
+      uint32_t e = eq_base + (before & 0xffffu);                      // keys == K before this thread
+      uint32_t pos = gt_base + (before >> 16) + min(e, remaining);
 #pragma unroll
       for (int i = 0; i < kTkPer; ++i) {
         const bool in = jt + i < n;
         const bool eq = in && cur[i] == K;
-        sel[i] = (in && cur[i] > K) || (eq && e < remaining);
+        const bool sel = (in && cur[i] > K) || (eq && e < remaining);
         e += eq ? 1u : 0u;
-        nsel += sel[i] ? 1u : 0u;
-      }
-      uint32_t pos = sel_base + wg_scan(nsel, 1, sel_all);
-#pragma unroll
-      for (int i = 0; i < kTkPer; ++i) {
-        if (sel[i]) {
+        if (sel) {
           if (pos < (uint32_t)k) orow[pos] = (int32_t)(lo + jt + i);   // exactly k are selected
           ++pos;
         }
       }
-      eq_base += eq_all;
-      sel_base += sel_all;
+      gt_base += all >> 16;
+      eq_base += all & 0xffffu;
 #pragma unroll
-      for (int i = 0; i < kTkPer; ++i) cur[i] = nxt[i];
+      for (int i = 0; i < kTkPer; ++i) {
+        cur[i] = nxt[i];
+        nxt[i] = nxt2[i];
+      }
     }
   };
   if (cached) compact(std::true_type{});
