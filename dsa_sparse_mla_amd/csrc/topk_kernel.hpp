@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
   // copy c of bin b at s_hist[hist_at(b, c)]: the copies of one bin fall in
   // eight different banks, and the 64 bins 4l + i that wave 0's lanes read
   // for one (i, c) spread over 16 banks
-  __shared__ uint32_t s_hist[256 * kTkCopies];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[256 * kTkCopies];   // 16-byte reads below
   __shared__ uint32_t s_wsum[2][kTkWaves];
   __shared__ uint32_t s_state[2];   // next byte's digit, keys still to take from it
 
@@ -166,10 +166,10 @@ __global__ void __launch_bounds__(kTkThreads) topk_select_kernel(const TopkArgs 
     else count(std::false_type{});
     __syncthreads();   // every wave's counts are in
     if (wave == 0) {
-      // lane l takes bins 4l .. 4l+3: their totals over the waves, the keys
-      // in higher bins (a suffix sum over the lanes), then the bin where the
-      // count from the top reaches `remaining`
-      // copy cp of bins 4l .. 4l+3 is four consecutive words (16-byte aligned)
+      // lane l takes bins 4l .. 4l+3: their totals over the copies (copy cp
+      // of the four bins is four consecutive words at a 16-byte boundary),
+      // the keys in higher bins (a suffix sum over the lanes), then the bin
+      // where the count from the top reaches `remaining`
       uint32_t c[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int cp = 0; cp < kTkCopies; ++cp) {
