@@ -461,22 +461,26 @@ def cpu_baseline_bwd(d, dout, budget_s: float):
 
 
 def gpu_info(dev):
-    """Device name, its maximum shader clock, and the current one as rocm-smi
-    reports it (best effort: a separate process, after the timed region)."""
-    import subprocess
+    """Device name, its maximum shader clock, and the current one as the
+    amdgpu driver reports it in sysfs (the level marked '*' in pp_dpm_sclk;
+    a file read, so nothing is started from this process)."""
+    import glob
     import torch
     p = torch.cuda.get_device_properties(dev)
     info = {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
             "sclk_max_mhz": round(getattr(p, "clock_rate", 0) / 1000) or None}
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        data = json.loads(r.stdout)
-        card = next(iter(data.values()))
-        sclk = card.get("sclk clock speed:") or card.get("sclk clock level:")
-        if sclk is not None:
-            info["sclk_now"] = sclk
-    except Exception:
-        pass
+    levels = []
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                cur = [ln.split(":", 1)[1].replace("*", "").strip() for ln in f if ln.rstrip().endswith("*")]
+            if cur:
+                levels.append(cur[0])
+        except (OSError, IndexError):
+            pass
+    if levels:
+        # one entry per card the host exposes; with one GPU there is one
+        info["sclk_now"] = levels[0] if len(set(levels)) == 1 else levels
     return info
 
 

@@ -431,18 +431,26 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
       constexpr int kVA = 4;   // operands read ahead (8 LDS operations)
       const uint32_t st = stage_of(t);
       const uint32_t pb = p_of(t);
+      // The first kEarly copies of the next gather go out before this wave's
+      // P and V^T reads: the LDS serves requests in arrival order, and the S
+      // waves' K reads at the same barrier are on the tile's critical path
+      // while these reads are not (the PV MFMAs fill the S waves' softmax tail).
+      constexpr int kEarly = 4;
       const int4 fl = *(const int4*)&s_flag[t & 1][0];
-      bf16x8_t pk[2][2];
-      read_p(pb, pk);
-      bf16x8_t vr[kVA + 1];
-#pragma unroll
-      for (int o = 0; o < kVA; ++o) vr[o] = vread(st, o & 3, o >> 2);
       uint32_t go[8];
       uint32_t gbase = 0;
       if (G) {
         gather_rows(tg, go, true);
         gbase = __builtin_amdgcn_readfirstlane(stage_of(tg));
+#pragma unroll
+        for (int d = 0; d < kEarly; ++d) gather_copy(gbase, go, d);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8_t pk[2][2];
+      read_p(pb, pk);
+      bf16x8_t vr[kVA + 1];
+#pragma unroll
+      for (int o = 0; o < kVA; ++o) vr[o] = vread(st, o & 3, o >> 2);
       if ((fl.x | fl.y | fl.z | fl.w) != 0) {   // settle step: new P, O factors
         __syncthreads();
         float al[2];
@@ -468,7 +476,7 @@ sparse_mla_fwd_ws_kernel(const FwdArgs a) {
         const int o = s >> 1, ht2 = s & 1;
         if (ht2 == 0 && o + kVA < kO) vr[(o + kVA) % (kVA + 1)] = vread(st, (o + kVA) & 3, (o + kVA) >> 2);
         oacc[ht2][o & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[o % (kVA + 1)], pk[ht2][o >> 2], oacc[ht2][o & 3], 0, 0, 0);
-        if (G && s < kDmaPerWave) gather_copy(gbase, go, s);
+        if (G && s + kEarly < kDmaPerWave) gather_copy(gbase, go, s + kEarly);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
